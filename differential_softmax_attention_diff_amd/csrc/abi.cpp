@@ -1,0 +1,213 @@
+// C-ABI entry points of libdiffattn: host-side argument checks, then kernel launches.
+//
+// Every check runs before anything is enqueued, and no HIP runtime call is made on an error
+// path, so invalid calls are safe (and testable) on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "diffattn.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxGridY = 65535;
+constexpr int kDecodeBlock = 256;  // keys per decode block; split chunks are multiples of it
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A 4-D (or 3-D) strided tensor argument: pointer present and 16-byte aligned, strides
+// non-negative and keeping every row start 16-byte aligned.
+da_status check_tensor(const da_tensor& t, int elem_bytes) {
+  if (t.ptr == nullptr || !aligned16(t.ptr)) return DA_ERR_NULL;
+  const int64_t q = 16 / elem_bytes;
+  if (t.sb < 0 || t.sh < 0 || t.sn < 0) return DA_ERR_SHAPE;
+  if (t.sb % q != 0 || t.sh % q != 0 || t.sn % q != 0) return DA_ERR_SHAPE;
+  return DA_OK;
+}
+
+da_status check_lambda(const da_lambda* lam, int32_t dl_expected_max) {
+  if (lam == nullptr) return DA_ERR_NULL;
+  if (lam->layer < 1) return DA_ERR_SHAPE;
+  if (lam->lambda_override == nullptr) {
+    if (!lam->lq1 || !lam->lk1 || !lam->lq2 || !lam->lk2) return DA_ERR_NULL;
+    if (lam->dl < 1 || lam->dl > dl_expected_max) return DA_ERR_SHAPE;
+  }
+  return DA_OK;
+}
+
+da::LambdaArgs lambda_args(const da_lambda* lam) {
+  da::LambdaArgs a;
+  a.lq1 = lam->lq1;
+  a.lk1 = lam->lk1;
+  a.lq2 = lam->lq2;
+  a.lk2 = lam->lk2;
+  a.dl = lam->dl;
+  a.lam_init = static_cast<float>(diffattn_lambda_init(lam->layer));
+  a.override_ = lam->lambda_override;
+  a.out = lam->lambda_out;
+  return a;
+}
+
+da::Strides strides(const da_tensor& t) { return da::Strides{t.sb, t.sh, t.sn}; }
+
+int decode_chunk(int32_t B, int32_t Hkv, int32_t L, int32_t num_splits) {
+  int splits = num_splits;
+  if (splits <= 0) {
+    // aim for >= 4096 workgroups over the 256 CUs, but keep >= one block per split
+    const int64_t bh = (int64_t)B * Hkv;
+    splits = (int)std::max<int64_t>(1, (4096 + bh - 1) / bh);
+  }
+  const int max_splits = (L + kDecodeBlock - 1) / kDecodeBlock;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int chunk = (L + splits - 1) / splits;
+  chunk = ((chunk + kDecodeBlock - 1) / kDecodeBlock) * kDecodeBlock;
+  return chunk;
+}
+
+da_status hip_status(hipError_t e) { return e == hipSuccess ? DA_OK : DA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+double diffattn_lambda_init(int32_t layer) {
+  if (layer < 1) return NAN;
+  return 0.8 - 0.6 * std::exp(-0.3 * (double)(layer - 1));
+}
+
+const char* diffattn_status_string(da_status s) {
+  switch (s) {
+    case DA_OK: return "DA_OK";
+    case DA_ERR_NULL: return "DA_ERR_NULL: required pointer is NULL or not 16-byte aligned";
+    case DA_ERR_SHAPE: return "DA_ERR_SHAPE: invalid sizes, strides, layer or eps";
+    case DA_ERR_UNSUPPORTED: return "DA_ERR_UNSUPPORTED: head width, dtype or head ratio not implemented";
+    case DA_ERR_WORKSPACE: return "DA_ERR_WORKSPACE: decode workspace missing or too small";
+    case DA_ERR_HIP: return "DA_ERR_HIP: HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+const char* diffattn_version(void) { return "diffattn-gfx950 0.1.0"; }
+
+da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2, da_tensor v,
+                          da_tensor out, int32_t B, int32_t H, int32_t N, int32_t d,
+                          da_dtype dtype, const da_lambda* lam, int32_t causal, float eps,
+                          uint32_t flags, void* stream) {
+  if (B < 0 || H < 0 || N < 0) return DA_ERR_SHAPE;
+  if (B == 0 || H == 0 || N == 0) return DA_OK;
+  if (dtype != DA_F32 && dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
+  if (d != 64) return d <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return DA_ERR_SHAPE;
+  if ((flags & ~DA_V1_NO_NORM) != 0u) return DA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > kMaxGridY || (N + 63) / 64 > kMaxGridY) return DA_ERR_UNSUPPORTED;
+  const int eb = dtype == DA_F32 ? 4 : 2;
+  for (const da_tensor* t : {&q1, &q2, &k1, &k2, &v, &out}) {
+    const da_status s = check_tensor(*t, eb);
+    if (s != DA_OK) return s;
+  }
+  da_status s = check_lambda(lam, 256);
+  if (s != DA_OK) return s;
+
+  da::PrefillParams p{};
+  p.q1 = q1.ptr; p.q2 = q2.ptr; p.k1 = k1.ptr; p.k2 = k2.ptr; p.v = v.ptr; p.out = out.ptr;
+  p.sq1 = strides(q1); p.sq2 = strides(q2); p.sk1 = strides(k1); p.sk2 = strides(k2);
+  p.sv = strides(v); p.so = strides(out);
+  p.B = B; p.heads = H; p.Hkv = H; p.N = N;
+  p.causal = causal ? 1 : 0;
+  p.norm = (flags & DA_V1_NO_NORM) ? 0 : 1;
+  p.scale = (float)(1.0 / std::sqrt((double)d));
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  p.eps = eps;
+  p.out_scale = (float)(1.0 - diffattn_lambda_init(lam->layer));
+  p.lam = lambda_args(lam);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == DA_F32) return hip_status(da::launch_v1_f32(p, st));
+  return hip_status(da::launch_v1_bf16(p, st));
+}
+
+da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor out,
+                          int32_t B, int32_t P, int32_t Hkv, int32_t N, int32_t D,
+                          da_dtype dtype, const da_lambda* lam, int32_t causal, void* stream) {
+  if (B < 0 || P < 0 || Hkv < 0 || N < 0) return DA_ERR_SHAPE;
+  if (B == 0 || P == 0 || N == 0) return DA_OK;
+  if (Hkv == 0) return DA_ERR_SHAPE;
+  if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
+  if (D != 128) return D <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+  if (P % Hkv != 0) return DA_ERR_SHAPE;
+  const int ppk = P / Hkv;
+  if (ppk > 8 || (N + 63) / 64 > kMaxGridY) return DA_ERR_UNSUPPORTED;
+  for (const da_tensor* t : {&q1, &q2, &k, &v, &out}) {
+    const da_status s = check_tensor(*t, 2);
+    if (s != DA_OK) return s;
+  }
+  da_status s = check_lambda(lam, 256);
+  if (s != DA_OK) return s;
+  const int ppw = (ppk % 2 == 0) ? 2 : 1;
+  const int64_t gx = (int64_t)B * Hkv * (ppk / ppw);
+  if (gx > (int64_t)INT32_MAX) return DA_ERR_UNSUPPORTED;
+
+  da::PrefillParams p{};
+  p.q1 = q1.ptr; p.q2 = q2.ptr; p.k1 = k.ptr; p.k2 = k.ptr; p.v = v.ptr; p.out = out.ptr;
+  p.sq1 = strides(q1); p.sq2 = strides(q2); p.sk1 = strides(k); p.sk2 = strides(k);
+  p.sv = strides(v); p.so = strides(out);
+  p.B = B; p.heads = P; p.Hkv = Hkv; p.N = N;
+  p.causal = causal ? 1 : 0;
+  p.norm = 0;
+  p.scale = (float)(1.0 / std::sqrt((double)D));
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  p.eps = 0.f;
+  p.out_scale = 1.f;
+  p.lam = lambda_args(lam);
+  return hip_status(da::launch_v2_bf16(p, ppw, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t diffattn_decode_workspace_bytes(int32_t B, int32_t P, int32_t Hkv, int32_t L, int32_t D,
+                                       int32_t num_splits) {
+  if (B <= 0 || P <= 0 || Hkv <= 0 || L <= 0 || D != 128 || P % Hkv != 0) return 0;
+  const int chunk = decode_chunk(B, Hkv, L, num_splits);
+  const int64_t splits = (L + chunk - 1) / chunk;
+  return (size_t)((int64_t)B * 2 * P * splits * (D + 2) * (int64_t)sizeof(float));
+}
+
+da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tensor vcache,
+                          da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t L, int32_t D,
+                          da_dtype dtype, const da_lambda* lam, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || P < 0 || Hkv < 0 || L < 0) return DA_ERR_SHAPE;
+  if (B == 0 || P == 0) return DA_OK;
+  if (L == 0 || Hkv == 0) return DA_ERR_SHAPE;  // the new token's own row is always present
+  if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
+  if (D != 128) return D <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+  if (P % Hkv != 0) return DA_ERR_SHAPE;
+  const int G = 2 * P / Hkv;
+  if (G != 2 && G != 4 && G != 8 && G != 16) return DA_ERR_UNSUPPORTED;
+  if (B > kMaxGridY || Hkv > kMaxGridY || P > INT32_MAX / 2) return DA_ERR_UNSUPPORTED;
+  for (const da_tensor* t : {&q1, &q2, &kcache, &vcache, &out}) {
+    const da_status s = check_tensor(*t, 2);
+    if (s != DA_OK) return s;
+  }
+  da_status s = check_lambda(lam, 256);
+  if (s != DA_OK) return s;
+  const size_t need = diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return DA_ERR_WORKSPACE;
+
+  da::DecodeParams p{};
+  p.q1 = q1.ptr; p.q2 = q2.ptr; p.k = kcache.ptr; p.v = vcache.ptr; p.out = out.ptr;
+  p.sq1 = strides(q1); p.sq2 = strides(q2); p.sk = strides(kcache); p.sv = strides(vcache);
+  p.so = strides(out);
+  p.B = B; p.P = P; p.Hkv = Hkv; p.L = L; p.D = D;
+  p.chunk = decode_chunk(B, Hkv, L, num_splits);
+  p.splits = (L + p.chunk - 1) / p.chunk;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  const int64_t n_rows = (int64_t)B * 2 * P * p.splits;
+  p.ws_acc = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_acc + n_rows * D;
+  p.lam = lambda_args(lam);
+  return hip_status(da::launch_decode_v2(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,274 @@
+// One V2 decode step for gfx950: every sequence's new query token attends to its whole KV cache.
+//
+// What is computed (ai-engineering.academy "Atención Diferencial (V2)", section "V1 vs V2: la
+// diferencia"): the two query heads (2p, 2p+1) of pair p read the same KV head
+// g = p * Hkv / P; out_p = softmax(q_2p K^T / sqrt(D)) V - lambda_p softmax(q_2p+1 K^T / sqrt(D)) V.
+// The page's point about V2 decode is that the KV cache is read once per step; here every K and V
+// byte is read exactly once per step, serving all 2P/Hkv query heads of its KV head.
+//
+// Bandwidth-bound design (split-K over the cache, then a log-sum-exp merge):
+//  * decode_partial: one 256-thread workgroup per (split s, KV head g, batch b) streams keys
+//    [s*chunk, min(L, (s+1)*chunk)) in blocks of 256 (64 per wavefront):
+//      - scores S = Q K^T with v_mfma_f32_16x16x32_bf16: the A operand holds the G query heads of
+//        the KV head (rows G..15 zero), the B operand takes K rows straight from global memory;
+//      - per-head block max / exp2 / sum by one wavefront per head over the 256 scores in LDS;
+//      - P.V on the vector ALUs: 16 lanes cover one 256-byte V row (8 channels each) and read the
+//        G weights of that key as an LDS broadcast;
+//    it writes the split's (running max, running sum, un-normalised accumulator) per query head.
+//  * decode_combine: per (pair, batch) merges the splits of both heads by log-sum-exp, normalises,
+//    and stores out = O_2p - lambda_p O_2p+1 in bf16.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace da {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kKB = 256;  // keys per block (64 per wavefront)
+constexpr int kThreads = 256;
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// G = query heads per KV head (2P / Hkv): 2, 4, 8 or 16.
+template <int G>
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
+  constexpr int SLOTS = (G + 3) / 4;  // heads whose softmax state one wavefront owns
+  __shared__ float sc_lds[G][kKB];    // scores of the block, per head
+  __shared__ __attribute__((aligned(16))) float pw_lds[kKB][G];  // exp-weights, per key
+  __shared__ float alpha_lds[G];
+  __shared__ float red_lds[4][G][kD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int k_begin = split * p.chunk;
+  const int k_end = min(p.L, k_begin + p.chunk);
+  const float c2 = p.scale_log2;
+
+  const bf16* kbase = static_cast<const bf16*>(p.k) + b * p.sk.sb + g * p.sk.sh;
+  const bf16* vbase = static_cast<const bf16*>(p.v) + b * p.sv.sb + g * p.sv.sh;
+
+  // A operand: row m = l16 is query head g*G + l16 (zero rows beyond G); k = 32t + 8*grp + i
+  bf16x8 qa[4];
+  {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    const int hq = g * G + l16;
+    const int pair = hq >> 1;
+    const bf16* qp = (hq & 1) ? static_cast<const bf16*>(p.q2) + b * p.sq2.sb + pair * p.sq2.sh
+                              : static_cast<const bf16*>(p.q1) + b * p.sq1.sb + pair * p.sq1.sh;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x4 x = l16 < G ? load16(qp + 32 * t + 8 * grp) : z;
+      qa[t] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  float mrun[SLOTS], lrun[SLOTS];
+#pragma unroll
+  for (int j = 0; j < SLOTS; ++j) {
+    mrun[j] = kNegBig;
+    lrun[j] = 0.f;
+  }
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+
+  for (int blk = k_begin; blk < k_end; blk += kKB) {
+    // issue this block's K and V loads up front
+    u32x4 kf[4][4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const int key = blk + 64 * w + 16 * sb + l16;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        kf[sb][t] = key < k_end ? load16(kbase + (int64_t)key * p.sk.sn + 32 * t + 8 * grp)
+                                : u32x4{0u, 0u, 0u, 0u};
+    }
+    u32x4 vf[16];
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int key = blk + 64 * w + 4 * st + grp;
+      vf[st] = key < k_end ? load16(vbase + (int64_t)key * p.sv.sn + 8 * l16) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // scores: D[m = head 4*grp + r][n = key l16] for 16 keys per MFMA group
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], __builtin_bit_cast(bf16x8, kf[sb][t]), s, 0, 0, 0);
+      const int kl = 64 * w + 16 * sb + l16;
+      const bool valid = blk + kl < k_end;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        if (h < G) sc_lds[h][kl] = valid ? s[r] : -INFINITY;
+      }
+    }
+    __syncthreads();
+
+    // per-head block softmax statistics (wavefront w owns heads w, w+4, ...)
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      const int h = w + 4 * j;
+      if (h < G) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = sc_lds[h][lane + 64 * i];
+        const float mx = wave_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const float mnew = fmaxf(mrun[j], mx);
+        const float alpha = exp2f((mrun[j] - mnew) * c2);
+        mrun[j] = mnew;
+        const float nm = -mnew * c2;
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(x[i], c2, nm));
+          pw_lds[lane + 64 * i][h] = e;
+          ls += e;
+        }
+        lrun[j] = lrun[j] * alpha + wave_sum(ls);
+        if (lane == 0) alpha_lds[h] = alpha;
+      }
+    }
+    __syncthreads();
+
+    // P.V: lane covers channels 8*l16 .. +7 of keys 64w + 4st + grp
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = alpha_lds[h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= a;
+    }
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int kl = 64 * w + 4 * st + grp;
+      float vv[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        vv[2 * m] = bf_lo(vf[st][m]);
+        vv[2 * m + 1] = bf_hi(vf[st][m]);
+      }
+      if constexpr (G >= 4) {
+#pragma unroll
+        for (int h4 = 0; h4 < G; h4 += 4) {
+          const f32x4 pw = *reinterpret_cast<const f32x4*>(&pw_lds[kl][h4]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h4 + r][e] = fmaf(pw[r], vv[e], acc[h4 + r][e]);
+        }
+      } else {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 pw = *reinterpret_cast<const f32x2*>(&pw_lds[kl][0]);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pw[r], vv[e], acc[r][e]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // reduce the four key groups of each wavefront, then the four wavefronts
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[h][e];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[h][e] = x;
+    }
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_lds[w][h][8 * l16 + e] = acc[h][e];
+  }
+  // softmax statistics of the split
+  const int two_p = 2 * p.P;
+#pragma unroll
+  for (int j = 0; j < SLOTS; ++j) {
+    const int h = w + 4 * j;
+    if (h < G && lane == 0) {
+      const int hq = g * G + h;
+      float* ml = p.ws_ml + (((int64_t)b * two_p + hq) * p.splits + split) * 2;
+      ml[0] = mrun[j];
+      ml[1] = lrun[j];
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * kD; idx += kThreads) {
+    const int h = idx / kD;
+    const int ch = idx % kD;
+    const float s = red_lds[0][h][ch] + red_lds[1][h][ch] + red_lds[2][h][ch] + red_lds[3][h][ch];
+    const int hq = g * G + h;
+    p.ws_acc[(((int64_t)b * two_p + hq) * p.splits + split) * kD + ch] = s;
+  }
+}
+
+__global__ __launch_bounds__(kD) void decode_combine_kernel(const DecodeParams p) {
+  const int pair = blockIdx.x;
+  const int b = blockIdx.y;
+  const int ch = threadIdx.x;
+  const int lane = ch & 63;
+  const float lam = head_lambda(p.lam, pair, lane);
+  if (p.lam.out != nullptr && b == 0 && ch == 0) p.lam.out[pair] = lam;
+  const int two_p = 2 * p.P;
+  float o[2];
+#pragma unroll
+  for (int br = 0; br < 2; ++br) {
+    const int hq = 2 * pair + br;
+    const float* ml = p.ws_ml + ((int64_t)b * two_p + hq) * p.splits * 2;
+    const float* ac = p.ws_acc + ((int64_t)b * two_p + hq) * p.splits * kD;
+    float m = kNegBig;
+    for (int s = 0; s < p.splits; ++s) m = fmaxf(m, ml[2 * s]);
+    float l = 0.f, x = 0.f;
+    for (int s = 0; s < p.splits; ++s) {
+      const float wgt = exp2f((ml[2 * s] - m) * p.scale_log2);
+      l = fmaf(ml[2 * s + 1], wgt, l);
+      x = fmaf(ac[(int64_t)s * kD + ch], wgt, x);
+    }
+    o[br] = x / l;
+  }
+  bf16* out = static_cast<bf16*>(p.out) + b * p.so.sb + pair * p.so.sh;
+  out[ch] = (bf16)(o[0] - lam * o[1]);
+}
+
+template <int G>
+hipError_t launch_partial(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.splits, p.Hkv, p.B);
+  hipLaunchKernelGGL(decode_partial_kernel<G>, grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_v2(const DecodeParams& p, hipStream_t stream) {
+  const int G = 2 * p.P / p.Hkv;
+  hipError_t e;
+  switch (G) {
+    case 2: e = launch_partial<2>(p, stream); break;
+    case 4: e = launch_partial<4>(p, stream); break;
+    case 8: e = launch_partial<8>(p, stream); break;
+    case 16: e = launch_partial<16>(p, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.P, p.B), dim3(kD), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace da

@@ -1,0 +1,65 @@
+// Plain-old-data parameter blocks handed from the C-ABI layer to the kernel launchers.
+// No HIP types here: the ABI layer and the kernels' translation units both include it.
+#pragma once
+#include <stdint.h>
+
+namespace da {
+
+// Lambda inputs of one call: four fp32 vectors per head (or head pair), the 1-based layer's
+// lambda_init, and the optional override / readback buffers (all device pointers).
+struct LambdaArgs {
+  const float* lq1;
+  const float* lk1;
+  const float* lq2;
+  const float* lk2;
+  int32_t dl;
+  float lam_init;
+  const float* override_;
+  float* out;
+};
+
+struct Strides {
+  int64_t sb, sh, sn;
+};
+
+// Prefill (V1 and V2).  For V1 `heads` is H and k2 is used; for V2 `heads` is the number of
+// pairs P, k1 == k2 == k, and q1 / q2 hold the even / odd query heads.
+struct PrefillParams {
+  const void* q1;
+  const void* q2;
+  const void* k1;
+  const void* k2;
+  const void* v;
+  void* out;
+  Strides sq1, sq2, sk1, sk2, sv, so;
+  int32_t B, heads, Hkv, N;
+  int32_t causal;
+  int32_t norm;          // V1: apply RMS norm + (1 - lambda_init) scale
+  int32_t n_row_blocks;  // query row blocks per (batch, head group)
+  int32_t groups_per_kv; // V2: workgroups per KV head along the pair axis
+  int32_t pairs_per_kv;  // V2: P / Hkv
+  float scale_log2;      // log2(e) / sqrt(d)
+  float scale;           // 1 / sqrt(d)
+  float eps;
+  float out_scale;       // 1 - lambda_init
+  LambdaArgs lam;
+};
+
+// One V2 decode step: split-K partial pass + combine pass.
+struct DecodeParams {
+  const void* q1;
+  const void* q2;
+  const void* k;
+  const void* v;
+  void* out;
+  Strides sq1, sq2, sk, sv, so;
+  int32_t B, P, Hkv, L, D;
+  int32_t splits;        // key-axis splits per (batch, KV head)
+  int32_t chunk;         // keys per split (multiple of the block size)
+  float scale_log2;
+  float* ws_acc;         // [B, 2P, splits, D]
+  float* ws_ml;          // [B, 2P, splits, 2]  (running max in score units, sum)
+  LambdaArgs lam;
+};
+
+}  // namespace da

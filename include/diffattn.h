@@ -1,0 +1,154 @@
+/*
+ * diffattn.h -- C ABI of the MI355X (gfx950) differential-attention forward library.
+ *
+ * Differential attention computes, for each head, two ordinary softmax maps
+ *   A1 = softmax(Q1 K1^T / sqrt(d)),   A2 = softmax(Q2 K2^T / sqrt(d))
+ * and returns (A1 - lambda * A2) V.  lambda is one learnable scalar per head,
+ *   lambda = exp(<lq1, lk1>) - exp(<lq2, lk2>) + lambda_init(l),
+ *   lambda_init(l) = 0.8 - 0.6 * exp(-0.3 * (l - 1))     (l = 1-based layer index).
+ * Sources: Ultralytics glossary "Differential Transformer", section "Cómo funciona la atención
+ * diferencial" (the two maps, their difference times V, the lambda schedule, per-head
+ * normalisation followed by the (1 - lambda_init) scale, half the heads with V twice as wide);
+ * ai-engineering.academy "Atención Diferencial (V2)", sections "La idea diferencial" (maps,
+ * difference, lambda from four vectors) and "V1 vs V2: la diferencia" (V2: doubled query heads
+ * over unchanged KV heads, outputs of a pair subtracted, no per-head RMSNorm; decode reads the
+ * KV cache once).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are described by da_tensor: a DEVICE pointer to element [0,0,0(,0)] and the
+ *    element strides of the batch, head and row axes.  The last axis is always contiguous
+ *    (stride 1) and must start 16-byte aligned in every row (strides multiples of 8 elements
+ *    for bf16, 4 for fp32).
+ *  - The caller owns every buffer.  The library allocates no device or host memory; the
+ *    decode path writes its split partials into a caller-provided device workspace.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
+ *    The library never synchronises; a result is valid once the stream has reached it.
+ *  - All argument checks run on the host before anything is enqueued.  On any error nothing
+ *    is launched and no output byte is written.  Empty problems (B == 0 or N/L == 0) return
+ *    DA_OK and enqueue nothing.  No entry point aborts, throws or prints.
+ *  - The library keeps no mutable global state; concurrent calls on different streams are
+ *    safe as long as their output/workspace buffers do not overlap.
+ *  - Causal masking: query row i sees key j iff j <= i (square problem, N queries, N keys).
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DA_OK = 0,
+  DA_ERR_NULL = 1,        /* a required pointer is NULL or not 16-byte aligned              */
+  DA_ERR_SHAPE = 2,       /* non-positive / inconsistent sizes or strides, layer < 1, eps<0 */
+  DA_ERR_UNSUPPORTED = 3, /* head width, dtype or head-count ratio not implemented          */
+  DA_ERR_WORKSPACE = 4,   /* decode workspace missing or smaller than required              */
+  DA_ERR_HIP = 5          /* a HIP runtime call or kernel launch reported an error          */
+} da_status;
+
+typedef enum { DA_F32 = 0, DA_BF16 = 1 } da_dtype;
+
+/* A strided 3-D or 4-D device tensor [batch, head, row, col]; col is contiguous. */
+typedef struct {
+  void* ptr;  /* device pointer to element [0,0,0,0]                                 */
+  int64_t sb; /* element stride between batches                                      */
+  int64_t sh; /* element stride between heads                                        */
+  int64_t sn; /* element stride between rows (ignored for the 3-D decode q/out)      */
+} da_tensor;
+
+/* Lambda parameters: four device fp32 vectors per head (V1) or per head pair (V2/decode),
+ * stored as row-major [n_lambda, dl] arrays (row h belongs to head/pair h). */
+typedef struct {
+  const float* lq1;
+  const float* lk1;
+  const float* lq2;
+  const float* lk2;
+  int32_t dl;                   /* length of each vector, 1..256                              */
+  int32_t layer;                /* 1-based layer index l of lambda_init(l)                    */
+  const float* lambda_override; /* nullable device fp32 [n_lambda]: use these lambdas instead */
+  float* lambda_out;            /* nullable device fp32 [n_lambda]: receives the lambdas used */
+} da_lambda;
+
+/* flags for diffattn_fwd_v1 */
+#define DA_V1_NO_NORM 1u /* return the core (A1 - lambda A2) V without RMS norm and scale */
+
+/*
+ * diffattn_fwd_v1 -- V1 layout (Ultralytics glossary "Differential Transformer", section
+ * "Cómo funciona la atención diferencial"): every head splits its query and key projections
+ * into two halves of width d and reads a value row twice as wide.
+ *
+ *   q1, q2, k1, k2 : [B, H, N, d]   (dtype)            V : [B, H, N, 2d]   (dtype)
+ *   out            : [B, H, N, 2d]  (dtype)            lambda vectors: [H, dl]
+ *   out[b,h,i,:] = (1 - lambda_init(l)) * O / sqrt(mean(O^2) + eps),
+ *   O = sum_j (A1[i,j] - lambda_h A2[i,j]) V[b,h,j,:]   (RMS over the 2d channels, no gain)
+ *   With flags & DA_V1_NO_NORM, out = O.
+ *
+ * Supported: d == 64; dtype DA_BF16 (bf16 in/out, fp32 accumulation, MFMA) or DA_F32
+ * (fp32 in/out, fp32 arithmetic).  Other d or dtypes return DA_ERR_UNSUPPORTED.
+ */
+da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2, da_tensor v,
+                          da_tensor out, int32_t B, int32_t H, int32_t N, int32_t d,
+                          da_dtype dtype, const da_lambda* lam, int32_t causal, float eps,
+                          uint32_t flags, void* stream);
+
+/*
+ * diffattn_fwd_v2 -- V2 layout (ai-engineering.academy "Atención Diferencial (V2)", sections
+ * "V1 vs V2: la diferencia" and "Ejercicios" 5): 2P query heads of full width D paired as
+ * (2p, 2p+1) over Hkv shared KV heads; pair p reads KV head p * Hkv / P.
+ *
+ *   q1 : [B, P, N, D]  query heads 2p   (e.g. a stride-2 view of a [B, 2P, N, D] tensor)
+ *   q2 : [B, P, N, D]  query heads 2p+1
+ *   k, v : [B, Hkv, N, D]                out : [B, P, N, D]       lambda vectors: [P, dl]
+ *   out[b,p,i,:] = softmax(q1 k^T / sqrt(D)) v - lambda_p softmax(q2 k^T / sqrt(D)) v
+ *   (no normalisation, no scale).
+ *
+ * Supported: D == 128, dtype DA_BF16, P % Hkv == 0, P / Hkv <= 8.
+ */
+da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor out,
+                          int32_t B, int32_t P, int32_t Hkv, int32_t N, int32_t D,
+                          da_dtype dtype, const da_lambda* lam, int32_t causal, void* stream);
+
+/*
+ * Bytes of device workspace diffattn_decode needs for these sizes and split count
+ * (num_splits <= 0 selects the library's default).  Returns 0 for unsupported sizes.
+ */
+size_t diffattn_decode_workspace_bytes(int32_t B, int32_t P, int32_t Hkv, int32_t L, int32_t D,
+                                       int32_t num_splits);
+
+/*
+ * diffattn_decode -- one V2 decode step (ai-engineering.academy "Atención Diferencial (V2)",
+ * section "V1 vs V2: la diferencia": the KV cache is read once per step for both heads of a
+ * pair).  Each sequence has one new query token whose own K/V already sits in cache row L-1;
+ * it attends to all L rows.
+ *
+ *   q1, q2 : [B, P, D]   (3-D: sb, sh used, sn ignored)     out : [B, P, D]
+ *   kcache, vcache : [B, Hkv, L, D]                        lambda vectors: [P, dl]
+ *   out[b,p,:] = last row of diffattn_fwd_v2 with N = L.
+ *   workspace: device buffer of at least diffattn_decode_workspace_bytes(...) bytes, 16-byte
+ *   aligned; its contents on entry do not matter and are clobbered.
+ *
+ * Supported: D == 128, dtype DA_BF16, P % Hkv == 0, 2P / Hkv <= 16.
+ */
+da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tensor vcache,
+                          da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t L, int32_t D,
+                          da_dtype dtype, const da_lambda* lam, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* lambda_init(l) = 0.8 - 0.6 exp(-0.3 (l - 1)) in double precision; NaN for l < 1. */
+double diffattn_lambda_init(int32_t layer);
+
+/* Static, human-readable name of a status code. */
+const char* diffattn_status_string(da_status status);
+
+/* Library version string. */
+const char* diffattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

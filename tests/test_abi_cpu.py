@@ -1,0 +1,138 @@
+"""CPU checks of the C ABI: the shared library loads, exports every function the header declares,
+and rejects invalid arguments on the host before touching the GPU (no compute calls here)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "diffattn.h")
+
+
+@pytest.fixture(scope="module")
+def da():
+    import differential_softmax_attention_diff_amd as mod
+
+    if not os.path.exists(mod.LIB_PATH):
+        pytest.fail("libdiffattn.so is not built (run __graft_entry__.build())")
+    mod.load_library()
+    return mod
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(diffattn_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported(da):
+    names = _declared_functions()
+    assert len(names) == 7, names
+    lib = ctypes.CDLL(da.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_lambda_init_helper_matches_oracle(da):
+    for l in range(1, 41):
+        assert da.diffattn_lambda_init(l) == pytest.approx(oracle.lambda_init(l), abs=1e-15)
+    assert math.isnan(da.diffattn_lambda_init(0))
+
+
+def test_status_strings(da):
+    for s in range(6):
+        assert da.diffattn_status_string(s).startswith(da.STATUS_NAMES[s])
+    assert "gfx950" in da.diffattn_version()
+
+
+def _t(ptr=0x10000, sb=0, sh=0, sn=64):
+    return da_mod().DaTensor(ptr, sb, sh, sn)
+
+
+def da_mod():
+    import differential_softmax_attention_diff_amd as mod
+    return mod
+
+
+def _lam(layer=1, dl=64, ptr=0x20000):
+    m = da_mod()
+    return m.DaLambda(ptr, ptr, ptr, ptr, dl, layer, None, None)
+
+
+def _v1(lib, ts, B=1, H=1, N=8, d=64, dt=1, lam=None, causal=1, eps=1e-5, flags=0):
+    lam = lam if lam is not None else _lam()
+    return lib.diffattn_fwd_v1(*ts, B, H, N, d, dt, ctypes.byref(lam), causal, eps, flags, None)
+
+
+def test_v1_host_validation(da):
+    lib = da.load_library()
+    good = [_t() for _ in range(6)]
+    assert _v1(lib, good, B=0) == 0                         # empty: OK, nothing enqueued
+    assert _v1(lib, good, N=0) == 0
+    assert _v1(lib, good, B=-1) == 2
+    assert _v1(lib, good, d=32) == 3                         # unsupported width
+    assert _v1(lib, good, d=0) == 2
+    assert _v1(lib, good, dt=7) == 3
+    assert _v1(lib, good, eps=-1.0) == 2
+    assert _v1(lib, good, eps=float("nan")) == 2
+    assert _v1(lib, good, flags=8) == 3
+    assert _v1(lib, good, lam=_lam(layer=0)) == 2
+    assert _v1(lib, good, lam=_lam(dl=0)) == 2
+    assert _v1(lib, good, lam=_lam(ptr=0)) == 1
+    bad = list(good)
+    bad[2] = _t(ptr=0)
+    assert _v1(lib, bad) == 1                                # NULL k1
+    bad[2] = _t(ptr=0x10008)
+    assert _v1(lib, bad) == 1                                # misaligned
+    bad[2] = _t(sn=63)
+    assert _v1(lib, bad) == 2                                # row stride breaks alignment
+    bad[2] = _t(sn=-64)
+    assert _v1(lib, bad) == 2
+    assert lib.diffattn_fwd_v1(*good, 1, 1, 8, 64, 1, None, 1, 1e-5, 0, None) == 1  # no lambda
+
+
+def test_v2_and_decode_host_validation(da):
+    lib = da.load_library()
+    t5 = [_t() for _ in range(5)]
+    lam = _lam(dl=128)
+    assert lib.diffattn_fwd_v2(*t5, 1, 3, 2, 8, 128, 1, ctypes.byref(lam), 1, None) == 2  # P % Hkv
+    assert lib.diffattn_fwd_v2(*t5, 1, 4, 2, 8, 64, 1, ctypes.byref(lam), 1, None) == 3   # D
+    assert lib.diffattn_fwd_v2(*t5, 1, 4, 2, 8, 128, 0, ctypes.byref(lam), 1, None) == 3  # fp32
+    assert lib.diffattn_fwd_v2(*t5, 1, 4, 0, 8, 128, 1, ctypes.byref(lam), 1, None) == 2
+    assert lib.diffattn_fwd_v2(*t5, 0, 4, 2, 8, 128, 1, ctypes.byref(lam), 1, None) == 0
+    assert lib.diffattn_fwd_v2(*t5, 1, 32, 2, 8, 128, 1, ctypes.byref(lam), 1, None) == 3  # 16 pairs/KV
+    need = da.diffattn_decode_workspace_bytes(2, 4, 2, 1000, 128)
+    assert need > 0
+    assert da.diffattn_decode_workspace_bytes(2, 3, 2, 1000, 128) == 0
+    dec = lambda ws, nbytes, P=4, Hkv=2, L=1000: lib.diffattn_decode(
+        *t5, 2, P, Hkv, L, 128, 1, ctypes.byref(lam), 0, ws, nbytes, None)
+    assert dec(None, need) == 4
+    assert dec(0x30000, need - 1) == 4
+    assert dec(0x30008, need) == 4                           # misaligned workspace
+    assert dec(0x30000, need, P=3) == 2
+    assert dec(0x30000, need, P=16, Hkv=1) == 3              # 32 query heads on one KV head
+    assert dec(0x30000, need, L=0) == 2
+
+
+def test_decode_workspace_size_formula(da):
+    # B * 2P * splits * (D + 2) floats; the split count never exceeds one per 256 keys
+    assert da.diffattn_decode_workspace_bytes(1, 1, 1, 100, 128, 0) == 1 * 2 * 1 * 130 * 4
+    # 3 requested splits -> chunks of ceil(1000 / 3) rounded up to 512 keys -> 2 splits
+    assert da.diffattn_decode_workspace_bytes(1, 1, 1, 1000, 128, 3) == 2 * 2 * 130 * 4
+    assert da.diffattn_decode_workspace_bytes(1, 1, 1, 1000, 128, 50) == 2 * 4 * 130 * 4
+    b = da.diffattn_decode_workspace_bytes(64, 16, 8, 32768, 128, 0)
+    assert b == 64 * 32 * 8 * 130 * 4
+
+
+def test_binding_refuses_cpu_tensors(da):
+    import torch
+
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    v = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        da.diffattn_fwd_v1(x, x, x, x, v, layer=1, out=v, lambda_override=None)

@@ -1,0 +1,97 @@
+"""GPU parity of the V2 prefill (paired query heads over shared GQA KV heads) against the float64
+CPU oracle.  V2 has no normalisation, so both sides are divided by the RMS of the oracle row
+before the bf16 tolerance (max |err| <= 2e-2, >= 99.9 % within 1e-2) is applied."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from oracle import compare
+from tests.helpers import dev, dev_lambda, f64, log, oracle_lambda, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def da():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import differential_softmax_attention_diff_amd as mod
+
+    mod.load_library()
+    return mod
+
+
+def _run_v2(da, t, layer, causal=True, lambda_out=None):
+    import torch
+
+    q = dev(t["q"])
+    lv = dev_lambda(t["lambda"][layer])
+    o = da.diffattn_fwd_v2(q[:, 0::2], q[:, 1::2], dev(t["k"]), dev(t["v"]), *lv, layer=layer,
+                           causal=causal, lambda_out=lambda_out)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy()
+
+
+def _oracle_v2(t, layer, causal=True, rows=None, pairs=None, batches=None):
+    lam = oracle_lambda(t["lambda"][layer], layer)
+    return oracle.diff_attn_v2(f64(t["q"]), f64(t["k"]), f64(t["v"]), lam, causal, rows=rows,
+                               pairs=pairs, batches=batches)
+
+
+@pytest.mark.parametrize("B,P,Hkv,N,causal", [
+    (1, 1, 1, 1, True),       # one pair per KV head (single-pair workgroups)
+    (1, 3, 3, 100, True),
+    (2, 2, 1, 64, False),     # two pairs per KV head
+    (1, 4, 2, 129, True),
+    (2, 8, 2, 200, True),     # four pairs per KV head
+    (1, 16, 8, 333, True),    # the workload's head layout at a short length
+    (1, 6, 2, 150, False),    # three pairs per KV head (odd: single-pair workgroups)
+])
+def test_v2_full_compare(da, B, P, Hkv, N, causal):
+    log(f"v2 B={B} P={P} Hkv={Hkv} N={N} causal={causal}")
+    t = wl.make_v2(B, P, Hkv, N, 128, "bf16", seed=N + 13 * P + Hkv, layers=(24,))
+    got = _run_v2(da, t, 24, causal)
+    ref = _oracle_v2(t, 24, causal)
+    st = compare.bf16_stats(got, ref, normalise=True)
+    assert compare.bf16_ok(st), st
+
+
+def test_v2_lambda_zero_is_even_heads_attention(da):
+    """lambda = 0 gives plain softmax attention of the even query heads."""
+    import torch
+
+    log("v2 lambda override 0")
+    t = wl.make_v2(1, 4, 2, 190, 128, "bf16", seed=77, layers=(24,))
+    q = dev(t["q"])
+    zero = torch.zeros(4, dtype=torch.float32, device="cuda")
+    o = da.diffattn_fwd_v2(q[:, 0::2], q[:, 1::2], dev(t["k"]), dev(t["v"]), layer=24,
+                           lambda_override=zero)
+    torch.cuda.synchronize()
+    ref = oracle.diff_attn_v2(f64(t["q"]), f64(t["k"]), f64(t["v"]), np.zeros(4), True)
+    st = compare.bf16_stats(o.float().cpu().numpy(), ref, normalise=True)
+    assert compare.bf16_ok(st), st
+
+
+def test_v2_workload_8k_sampled_rows(da):
+    """Full V2 prefill workload (B=2, 32 query heads / 16 pairs over 8 KV heads, D=128, N=8192,
+    causal, l=24), checked on sampled rows of several pairs."""
+    import torch
+
+    cfg, t = wl.make("v2_prefill_8k")
+    layer = cfg["layers"][0]
+    log("v2 B=2 P=16 Hkv=8 N=8192 (full launch, sampled rows)")
+    lam_out = torch.full((16,), float("nan"), dtype=torch.float32, device="cuda")
+    got = _run_v2(da, t, layer, lambda_out=lam_out)
+    assert np.isfinite(got).all()
+    lam = oracle_lambda(t["lambda"][layer], layer)
+    np.testing.assert_allclose(lam_out.cpu().numpy(), lam, rtol=0, atol=2e-6)
+    rows = sample_rows(8192, 64, seed=3, extra=(0, 1, 63, 64, 8190, 8191))
+    for b in (0, 1):
+        for p in (0, 7, 15):
+            ref = _oracle_v2(t, layer, rows=rows, pairs=[p], batches=[b])[0, 0]
+            st = compare.bf16_stats(got[b, p, rows], ref, normalise=True)
+            assert compare.bf16_ok(st), (b, p, st)
