@@ -1,0 +1,299 @@
+"""Benchmark of the differential-attention forward path on one MI355X.
+
+A step is one pass of the hot path over one batch of seeded synthetic input already resident in
+HBM.  The headline workload is the V1 prefill at a 4K context (B=4, H=16, N=4096, d=64, V width
+128, causal, bf16 in / fp32 accumulate, layer 12); its line carries the MFMA roofline and the CPU
+oracle baseline.  The V2 prefill (B=2, 32 query heads / 16 pairs over 8 KV heads, D=128, N=8192)
+and the V2 decode step (B=64, 32 query / 8 KV heads, D=128, 32K-token cache) are reported in the
+same JSON line under "secondary", each with its own roofline.
+
+FLOP and byte conventions (per launch):
+  V1 prefill  algorithmic flops  = B*H * 8*d * Np      (two QK^T products + one (A1-lambda A2)V)
+              executed MFMA flops = B*H * 12*d * Np    (two QK^T + two P.V in one fused pass)
+  V2 prefill  algorithmic flops  = B*P * 6*D * Np,  executed = B*P * 8*D * Np
+  decode      algorithmic bytes  = K and V cache + queries + output (every byte read once)
+with Np = N(N+1)/2 causal query-key pairs.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--only v1|v2|decode]
+       [--no-cpu-baseline] [--cpu-seconds S]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "diff-attn fwd TFLOP/s (% bf16 MFMA peak); decode HBM GB/s (% of 8 TB/s)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "prefill": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "prefill_bf16.hip"),
+    "decode": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "decode_v2.hip"),
+}
+
+
+def source_hash(kind: str) -> str:
+    with open(KERNEL_SOURCES[kind], "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(key: str, kind: str):
+    """HBM bytes per launch from the committed counter run, or None if the kernel has changed."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(key)
+    if not ent or ent.get("source_hash") != source_hash(kind):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def to_dev(x, torch):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Average milliseconds per call, HIP events on the stream the kernels are launched on."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def causal_pairs(n):
+    return n * (n + 1) // 2
+
+
+# ------------------------------------------------------------------------------------------------
+# workloads
+# ------------------------------------------------------------------------------------------------
+
+def bench_v1(da, torch, steps, warmup):
+    cfg, t = wl.make("v1_prefill_4k")
+    layer = cfg["layers"][0]
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    args = [to_dev(t[k], torch) for k in ("q1", "q2", "k1", "k2", "v")]
+    lv = [torch.from_numpy(x).to("cuda") for x in t["lambda"][layer]]
+    out = torch.empty((B, H, N, 2 * d), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: da.diffattn_fwd_v1(*args, *lv, layer=layer, out=out)
+    ms = time_launches(fn, steps, warmup, torch)
+    npairs = causal_pairs(N)
+    f_alg = B * H * 8 * d * npairs
+    f_exec = B * H * 12 * d * npairs
+    tf_alg = f_alg / (ms * 1e-3) / 1e12
+    tf_exec = f_exec / (ms * 1e-3) / 1e12
+    res = {
+        "workload": "v1_prefill_4k", "ms": ms, "tflops_alg": tf_alg, "tflops_exec": tf_exec,
+        "config": {"workload": "v1_prefill_4k", "B": B, "H": H, "N": N, "d": d, "dv": 2 * d,
+                   "causal": True, "layer": layer, "dtype": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(tf_alg, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_alg / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("v1_prefill_4k", "prefill"),
+                     "executed_mfma_tflops": round(tf_exec, 2),
+                     "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
+                     "kernel": "prefill_kernel<64,false,1,false>"},
+    }
+    return res, (cfg, t)
+
+
+def bench_v2(da, torch, steps, warmup):
+    cfg, t = wl.make("v2_prefill_8k")
+    layer = cfg["layers"][0]
+    B, P, Hkv, N, D = cfg["B"], cfg["P"], cfg["Hkv"], cfg["N"], cfg["D"]
+    q = to_dev(t["q"], torch)
+    k, v = to_dev(t["k"], torch), to_dev(t["v"], torch)
+    lv = [torch.from_numpy(x).to("cuda") for x in t["lambda"][layer]]
+    out = torch.empty((B, P, N, D), dtype=torch.bfloat16, device="cuda")
+    q1, q2 = q[:, 0::2], q[:, 1::2]
+    fn = lambda: da.diffattn_fwd_v2(q1, q2, k, v, *lv, layer=layer, out=out)
+    ms = time_launches(fn, steps, warmup, torch)
+    npairs = causal_pairs(N)
+    f_alg = B * P * 6 * D * npairs
+    f_exec = B * P * 8 * D * npairs
+    tf_alg = f_alg / (ms * 1e-3) / 1e12
+    tf_exec = f_exec / (ms * 1e-3) / 1e12
+    return {
+        "workload": "v2_prefill_8k", "ms": ms, "value": round(tf_alg, 2), "unit": "TFLOP/s",
+        "config": {"workload": "v2_prefill_8k", "B": B, "P": P, "query_heads": 2 * P, "Hkv": Hkv,
+                   "N": N, "D": D, "causal": True, "layer": layer, "dtype": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(tf_alg, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_alg / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("v2_prefill_8k", "prefill"),
+                     "executed_mfma_tflops": round(tf_exec, 2),
+                     "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
+                     "kernel": "prefill_kernel<128,true,2,true>"},
+    }
+
+
+def bench_decode(da, torch, steps, warmup):
+    cfg, t = wl.make("v2_decode_32k")
+    layer = cfg["layers"][0]
+    B, P, Hkv, L, D = cfg["B"], cfg["P"], cfg["Hkv"], cfg["L"], cfg["D"]
+    q = to_dev(t["q"], torch)
+    kc, vc = to_dev(t["kcache"], torch), to_dev(t["vcache"], torch)
+    del t["kcache"], t["vcache"]
+    lv = [torch.from_numpy(x).to("cuda") for x in t["lambda"][layer]]
+    out = torch.empty((B, P, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(da.diffattn_decode_workspace_bytes(B, P, Hkv, L, D), dtype=torch.uint8,
+                     device="cuda")
+    q1, q2 = q[:, 0::2], q[:, 1::2]
+    fn = lambda: da.diffattn_decode(q1, q2, kc, vc, *lv, layer=layer, out=out, workspace=ws)
+    ms = time_launches(fn, steps, warmup, torch)
+    nbytes = 2 * B * Hkv * L * D * 2 + B * 2 * P * D * 2 + B * P * D * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": "v2_decode_32k", "ms": ms, "value": round(gbs, 1), "unit": "GB/s",
+        "config": {"workload": "v2_decode_32k", "B": B, "P": P, "query_heads": 2 * P, "Hkv": Hkv,
+                   "L": L, "D": D, "layer": layer, "dtype": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("v2_decode_32k", "decode"),
+                     "algorithmic_bytes": nbytes,
+                     "kernel": "decode_partial_kernel<4> + decode_combine_kernel (whole step)"},
+    }
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the V1 workload)
+# ------------------------------------------------------------------------------------------------
+
+def cpu_baseline(cfg, t, budget_s):
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    layer = cfg["layers"][0]
+    lam = oracle.lambda_value(*t["lambda"][layer], layer)
+    lam_init = oracle.lambda_init(layer)
+    N, d = cfg["N"], cfg["d"]
+    f32 = lambda x: wl.as_f32(x, "bf16")
+    done_heads = 0
+    flops = 0
+    t0 = time.perf_counter()
+    # whole heads, one (batch, head) after another, until the time budget is used
+    for b in range(cfg["B"]):
+        for h in range(cfg["H"]):
+            sl = lambda x: f32(x[b:b + 1, h:h + 1])
+            oracle.diff_attn_v1(sl(t["q1"]), sl(t["q2"]), sl(t["k1"]), sl(t["k2"]), sl(t["v"]),
+                                lam[h:h + 1], lam_init, True, cfg["eps"])
+            done_heads += 1
+            flops += 8 * d * causal_pairs(N)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done_heads} of {cfg['B'] * cfg['H']} (batch, head) slices, all {N} causal "
+                      f"rows each, of the V1 4K workload; float64 numpy oracle, {el:.1f} s"}
+
+
+# ------------------------------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["v1", "v2", "decode"], default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for "
+              f"--gpus {a.gpus}); the per-GPU kernel is what one GPU shows.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import differential_softmax_attention_diff_amd as da
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    da.load_library()
+
+    if a.copy_calibration:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 3}), flush=True)
+        return
+
+    secondary = []
+    if a.only in (None, "v2"):
+        print("[bench] v2 prefill", file=sys.stderr, flush=True)
+        secondary.append(bench_v2(da, torch, a.steps, a.warmup))
+        torch.cuda.empty_cache()
+    if a.only in (None, "decode"):
+        print("[bench] v2 decode", file=sys.stderr, flush=True)
+        secondary.append(bench_decode(da, torch, a.steps, a.warmup))
+        torch.cuda.empty_cache()
+    if a.only == "v1" or a.only is None:
+        print("[bench] v1 prefill", file=sys.stderr, flush=True)
+        head, (cfg, t) = bench_v1(da, torch, a.steps, a.warmup)
+    else:
+        head = secondary.pop(0)
+        head["tflops_alg"] = head["value"]
+        cfg, t = None, None
+
+    line = {
+        "metric": METRIC,
+        "value": round(head.get("tflops_alg", head.get("value")), 2),
+        "unit": head["roofline"]["unit"],
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(head["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 activations, lambda vectors N(0, 0.1^2)",
+        "config": head["config"],
+        "roofline": head["roofline"],
+    }
+    if cfg is not None and not a.no_cpu_baseline:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, t, a.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    line["secondary"] = [{k: v for k, v in s.items() if k != "ms"} | {"ms_per_step": round(s["ms"], 4)}
+                         for s in secondary]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

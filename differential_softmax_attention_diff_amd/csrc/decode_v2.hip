@@ -28,9 +28,6 @@ constexpr int kKB = 256;  // keys per block (64 per wavefront)
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-
 // G = query heads per KV head (2P / Hkv): 2, 4, 8 or 16.
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
@@ -157,8 +154,8 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
       float vv[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        vv[2 * m] = bf_lo(vf[st][m]);
-        vv[2 * m + 1] = bf_hi(vf[st][m]);
+        vv[2 * m] = bf16_lo(vf[st][m]);
+        vv[2 * m + 1] = bf16_hi(vf[st][m]);
       }
       if constexpr (G >= 4) {
 #pragma unroll

@@ -61,12 +61,31 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16& s, int base) {
   return r;
 }
 
-template <int DQK, bool V2, int PPW>
+__device__ __forceinline__ f16x8 cvt8h(const f32x16& s, int base) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (_Float16)s[base + i];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  f16x2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Largest magnitude an fp16 operand may take without overflowing.
+constexpr float kF16Max = 65504.f;
+
+// F16PV: the P.V product runs on the fp16 MFMA (P and V rounded to fp16, 11 significant bits,
+// instead of bf16's 8).  A V tile holding any |v| > 65504 is staged and multiplied in bf16
+// instead, decided by a workgroup-wide vote, so no input range is lost.
+template <int DQK, bool V2, int PPW, bool F16PV>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p) {
   using C = Cfg<DQK, V2>;
   constexpr int WPP = V2 ? 4 / PPW : 4;  // wavefronts per head (pair)
   constexpr int BM = 32 * WPP;           // query rows per workgroup
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+  __shared__ int vote[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     }
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, bool big) {
     bf16* st = smem + buf * C::STAGE;
 #pragma unroll
     for (int nk = 0; nk < C::NK; ++nk) {
@@ -171,12 +190,39 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     for (int m = 0; m < 4; ++m) {
       const uint32_t w0 = vreg[0][m], w1 = vreg[1][m], w2 = vreg[2][m], w3 = vreg[3][m];
       u32x2 lo, hi;  // channel 2m (low halves) and 2m+1 (high halves)
-      lo[0] = (w0 & 0xffffu) | (w1 << 16);
-      lo[1] = (w2 & 0xffffu) | (w3 << 16);
-      hi[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-      hi[1] = (w2 >> 16) | (w3 & 0xffff0000u);
+      if (F16PV && !big) {
+        lo[0] = pack_h2(bf16_lo(w0), bf16_lo(w1));
+        lo[1] = pack_h2(bf16_lo(w2), bf16_lo(w3));
+        hi[0] = pack_h2(bf16_hi(w0), bf16_hi(w1));
+        hi[1] = pack_h2(bf16_hi(w2), bf16_hi(w3));
+      } else {
+        lo[0] = (w0 & 0xffffu) | (w1 << 16);
+        lo[1] = (w2 & 0xffffu) | (w3 << 16);
+        hi[0] = (w0 >> 16) | (w1 & 0xffff0000u);
+        hi[1] = (w2 >> 16) | (w3 & 0xffff0000u);
+      }
       *reinterpret_cast<u32x2*>(vt + (8 * v_cc + 2 * m) * C::VSTR + pos) = lo;
       *reinterpret_cast<u32x2*>(vt + (8 * v_cc + 2 * m + 1) * C::VSTR + pos) = hi;
+    }
+  };
+
+  // Workgroup-wide vote: does the staged V tile hold a value fp16 cannot represent?
+  // (Called by every thread between two barriers; returns the same answer everywhere.)
+  auto vote_big = [&]() -> bool {
+    if constexpr (!F16PV) {
+      return true;
+    } else {
+      float mx = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(vreg[r][m])), fabsf(bf16_hi(vreg[r][m]))));
+      const bool any = __any(mx > kF16Max);
+      if (lane == 0) vote[w] = any ? 1 : 0;
+      __syncthreads();
+      const bool big = (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+      return big;
     }
   };
 
@@ -193,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
   const float sl2 = p.scale_log2;
   const bool wave_has_rows = wrow < N;
 
-  auto compute_tile = [&](int buf, int kt) {
+  auto compute_tile = [&](int buf, int kt, bool big) {
     if (!wave_has_rows) return;
     if (p.causal && kt > wrow + 31) return;  // every key of the tile is in this wave's future
     const bf16* st = smem + buf * C::STAGE;
@@ -233,8 +279,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
         }
     }
 
-    // online softmax per branch; P^T operands in bf16
-    bf16x8 pb[2][2][2];
+    // online softmax per branch (P is left in s as fp32)
 #pragma unroll
     for (int br = 0; br < 2; ++br) {
       float mx = s[br][0][0];
@@ -259,36 +304,65 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
       lrun[br] = lrun[br] * alpha + ls;
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[br][db] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        pb[br][kb][0] = cvt8(s[br][kb], 0);
-        pb[br][kb][1] = cvt8(s[br][kb], 8);
-      }
     }
 
     // O^T += V^T P^T for both branches (the V^T operand is shared)
+    if (F16PV && !big) {
+      f16x8 ph[2][2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int br = 0; br < 2; ++br)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x8 a = lds_read8(vt + (db * 32 + c) * C::VSTR + kb * 32 + 16 * u + 8 * hh);
-          acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][kb][u], acc[0][db], 0, 0, 0);
-          acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][kb][u], acc[1][db], 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb) {
+          ph[br][kb][0] = cvt8h(s[br][kb], 0);
+          ph[br][kb][1] = cvt8h(s[br][kb], 8);
         }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const f16x8 a = *reinterpret_cast<const f16x8*>(vt + (db * 32 + c) * C::VSTR + kb * 32 + 16 * u + 8 * hh);
+            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[0][kb][u], acc[0][db], 0, 0, 0);
+            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[1][kb][u], acc[1][db], 0, 0, 0);
+          }
+    } else {
+      bf16x8 pb[2][2][2];
+#pragma unroll
+      for (int br = 0; br < 2; ++br)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          pb[br][kb][0] = cvt8(s[br][kb], 0);
+          pb[br][kb][1] = cvt8(s[br][kb], 8);
+        }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const bf16x8 a = lds_read8(vt + (db * 32 + c) * C::VSTR + kb * 32 + 16 * u + 8 * hh);
+            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][kb][u], acc[0][db], 0, 0, 0);
+            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][kb][u], acc[1][db], 0, 0, 0);
+          }
+    }
   };
 
-  // ---- main loop: one barrier per tile
+  // ---- main loop: one barrier per tile (plus the vote's barrier on the fp16 path)
   if (ntiles > 0) {
     load_tile(0);
-    store_tile(0);
+    bool big_cur = vote_big();
+    store_tile(0, big_cur);
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
       const bool more = it + 1 < ntiles;
       if (more) load_tile((it + 1) * kBN);
-      compute_tile(it & 1, it * kBN);
-      if (more) store_tile((it + 1) & 1);
+      compute_tile(it & 1, it * kBN, big_cur);
+      if (more) {
+        const bool big_next = vote_big();
+        store_tile((it + 1) & 1, big_next);
+        big_cur = big_next;
+      }
       __syncthreads();
     }
   }
@@ -334,7 +408,7 @@ hipError_t launch_v1_bf16(const PrefillParams& p, hipStream_t stream) {
   PrefillParams q = p;
   q.n_row_blocks = (p.N + 127) / 128;
   const dim3 grid(p.B * p.heads, q.n_row_blocks);
-  hipLaunchKernelGGL((prefill_kernel<64, false, 1>), grid, dim3(kThreads), 0, stream, q);
+  hipLaunchKernelGGL((prefill_kernel<64, false, 1, false>), grid, dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 
@@ -345,12 +419,12 @@ hipError_t launch_v2_bf16(const PrefillParams& p, int pairs_per_wg, hipStream_t 
     q.groups_per_kv = q.pairs_per_kv / 2;
     q.n_row_blocks = (p.N + 63) / 64;
     const dim3 grid(p.B * p.Hkv * q.groups_per_kv, q.n_row_blocks);
-    hipLaunchKernelGGL((prefill_kernel<128, true, 2>), grid, dim3(kThreads), 0, stream, q);
+    hipLaunchKernelGGL((prefill_kernel<128, true, 2, true>), grid, dim3(kThreads), 0, stream, q);
   } else {
     q.groups_per_kv = q.pairs_per_kv;
     q.n_row_blocks = (p.N + 127) / 128;
     const dim3 grid(p.B * p.Hkv * q.groups_per_kv, q.n_row_blocks);
-    hipLaunchKernelGGL((prefill_kernel<128, true, 1>), grid, dim3(kThreads), 0, stream, q);
+    hipLaunchKernelGGL((prefill_kernel<128, true, 1, true>), grid, dim3(kThreads), 0, stream, q);
   }
   return hipGetLastError();
 }

@@ -52,6 +52,7 @@ def test_decode_full_compare(da, B, P, Hkv, L, splits):
     lam = oracle_lambda(t["lambda"][24], 24)
     ref = oracle.diff_decode_v2(f64(t["q"]), f64(t["kcache"]), f64(t["vcache"]), lam)
     st = compare.bf16_stats(got, ref, normalise=True)
+    log(f"  stats {st}")
     assert compare.bf16_ok(st), st
 
 
@@ -79,8 +80,9 @@ def test_decode_matches_prefill_last_row(da):
     torch.cuda.synchronize()
     a = pre[:, :, -1].float().cpu().numpy()
     b = dec.float().cpu().numpy()
+    # two bf16 results, each within 2e-2 (relative to the row RMS) of the exact value
     rms = np.sqrt(np.mean(a * a, axis=-1, keepdims=True))
-    assert np.max(np.abs(a - b) / rms) < 2e-2
+    assert np.max(np.abs(a - b) / rms) < 4e-2
 
 
 @pytest.mark.timeout(900)
@@ -96,4 +98,5 @@ def test_decode_workload_32k_sampled_batches(da):
     bs = [0, 17, 63]
     ref = oracle.diff_decode_v2(f64(t["q"][bs]), f64(t["kcache"][bs]), f64(t["vcache"][bs]), lam)
     st = compare.bf16_stats(got[bs], ref, normalise=True)
+    log(f"  stats {st}")
     assert compare.bf16_ok(st), st

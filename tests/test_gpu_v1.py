@@ -55,6 +55,7 @@ def test_v1_fp32_small_workload_all_layers(da):
         got = _run_v1(da, t, "f32", layer)
         ref = _oracle_v1(t, "f32", layer)
         err = compare.row_rel_error(got, ref)
+        log(f"  row-relative error {err:.3e}")
         assert err <= compare.FP32_ROW_REL_TOL, (layer, err)
 
 
@@ -81,6 +82,7 @@ def test_v1_bf16_full_compare(da, B, H, N, causal):
     got = _run_v1(da, t, "bf16", 12, causal=causal)
     ref = _oracle_v1(t, "bf16", 12, causal=causal)
     st = compare.bf16_stats(got, ref)
+    log(f"  stats {st}")
     assert compare.bf16_ok(st), st
 
 
@@ -122,6 +124,7 @@ def test_v1_bf16_workload_4k_sampled_rows(da):
         for h in (0, 5, 15):
             ref = _oracle_v1(t, "bf16", layer, rows=rows, heads=[h], batches=[b])[0, 0]
             st = compare.bf16_stats(got[b, h, rows], ref)
+            log(f"  b={b} h={h} stats {st}")
             assert compare.bf16_ok(st), (b, h, st)
 
 
@@ -138,4 +141,5 @@ def test_v1_bf16_long_context_128k_needles(da):
         for h in (0, 9):
             ref = _oracle_v1(t, "bf16", layer, rows=rows, heads=[h], batches=[0])[0, 0]
             st = compare.bf16_stats(got[0, h, rows], ref)
+            log(f"  layer={layer} h={h} stats {st}")
             assert compare.bf16_ok(st), (layer, h, st)

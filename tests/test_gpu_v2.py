@@ -57,7 +57,38 @@ def test_v2_full_compare(da, B, P, Hkv, N, causal):
     got = _run_v2(da, t, 24, causal)
     ref = _oracle_v2(t, 24, causal)
     st = compare.bf16_stats(got, ref, normalise=True)
+    log(f"  stats {st}")
     assert compare.bf16_ok(st), st
+
+
+def test_v2_values_beyond_fp16_range(da):
+    """P.V runs in fp16 except for V tiles holding a value fp16 cannot represent; those tiles
+    take the bf16 MFMA.  Plant such values in a few tiles and bound every output element by the
+    componentwise error of bf16 weights: |err| <= 2^-8 (|A_a| |V| + |lambda| |A_b| |V|) + 2^-8 |ref|.
+    (Large planted values make O_a - lambda O_b cancel, so a row-RMS normalised check would be
+    ill-conditioned here; an fp16 overflow or saturation of +-1e5 would exceed this bound by far.)"""
+    log("v2 with |v| > 65504 in some tiles")
+    N = 300
+    t = wl.make_v2(1, 2, 1, N, 128, "bf16", seed=31, layers=(24,))
+    vf = wl.as_f32(t["v"], "bf16").copy()
+    vf[0, 0, 5, 7] = 1.0e5        # tile 0
+    vf[0, 0, 130, 64] = -3.0e5    # tile 2
+    vf[0, 0, 299, 127] = 7.0e4    # last, ragged tile
+    t["v"] = wl.f32_to_bf16_bits(vf)
+    got = _run_v2(da, t, 24, True)
+    assert np.isfinite(got).all()
+    ref = _oracle_v2(t, 24, True)
+    lam = oracle_lambda(t["lambda"][24], 24)
+    q, k, v = f64(t["q"]), f64(t["k"])[0, 0], f64(t["v"])[0, 0]
+    worst = 0.0
+    for p in range(2):
+        a1, a2, _ = oracle.diff_maps(q[0, 2 * p], k, q[0, 2 * p + 1], k, lam[p], True)
+        mag = np.abs(a1) @ np.abs(v) + abs(lam[p]) * (np.abs(a2) @ np.abs(v))
+        err = np.abs(got[0, p] - ref[0, p])
+        bound = 2.0 ** -8 * (mag + np.abs(ref[0, p]))
+        worst = max(worst, float(np.max(err / bound)))
+    log(f"  worst err / bound = {worst:.3f}")
+    assert worst <= 1.0
 
 
 def test_v2_lambda_zero_is_even_heads_attention(da):
@@ -94,4 +125,5 @@ def test_v2_workload_8k_sampled_rows(da):
         for p in (0, 7, 15):
             ref = _oracle_v2(t, layer, rows=rows, pairs=[p], batches=[b])[0, 0]
             st = compare.bf16_stats(got[b, p, rows], ref, normalise=True)
+            log(f"  b={b} p={p} stats {st}")
             assert compare.bf16_ok(st), (b, p, st)
