@@ -20,6 +20,9 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libdiffattn.so")
 
 SOURCES = ["abi.cpp", "fwd_v1_f32.hip", "prefill_bf16.hip", "decode_v2.hip"]
+# Per-source extra flags.  The prefill kernels keep their MFMA accumulators in VGPRs: the online
+# softmax rescales them with vector ALU ops, and AGPR-resident accumulators cost a copy per use.
+EXTRA_FLAGS = {"prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -56,7 +59,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max(1, jobs)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"

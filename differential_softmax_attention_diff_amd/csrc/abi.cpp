@@ -53,6 +53,12 @@ da::LambdaArgs lambda_args(const da_lambda* lam) {
 
 da::Strides strides(const da_tensor& t) { return da::Strides{t.sb, t.sh, t.sn}; }
 
+// The bf16 prefill addresses each head slice with 32-bit byte offsets (buffer loads whose range
+// check zero-fills rows past N), so a slice of N + 256 rows must span less than 4 GiB.
+bool rows_fit_32bit(const da_tensor& t, int32_t N, int elem_bytes) {
+  return ((int64_t)N + 256) * t.sn * elem_bytes < ((int64_t)1 << 32);
+}
+
 int decode_chunk(int32_t B, int32_t Hkv, int32_t L, int32_t num_splits) {
   int splits = num_splits;
   if (splits <= 0) {
@@ -126,6 +132,8 @@ da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2
   p.lam = lambda_args(lam);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dtype == DA_F32) return hip_status(da::launch_v1_f32(p, st));
+  for (const da_tensor* t : {&q1, &q2, &k1, &k2, &v})
+    if (!rows_fit_32bit(*t, N, 2)) return DA_ERR_UNSUPPORTED;
   return hip_status(da::launch_v1_bf16(p, st));
 }
 
@@ -146,6 +154,8 @@ da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, 
   }
   da_status s = check_lambda(lam, 256);
   if (s != DA_OK) return s;
+  for (const da_tensor* t : {&q1, &q2, &k, &v})
+    if (!rows_fit_32bit(*t, N, 2)) return DA_ERR_UNSUPPORTED;
   const int ppw = (ppk % 2 == 0) ? 2 : 1;
   const int64_t gx = (int64_t)B * Hkv * (ppk / ppw);
   if (gx > (int64_t)INT32_MAX) return DA_ERR_UNSUPPORTED;

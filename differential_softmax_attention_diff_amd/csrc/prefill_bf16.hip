@@ -11,21 +11,30 @@
 // Design (one pass over K/V per query block):
 //  * A 256-thread workgroup owns a block of query rows; each of its four wavefronts owns 32 query
 //    rows (V1: 4 x 32 rows of one head; V2: 2 pairs x 2 x 32 rows, or 1 pair x 4 x 32 rows).
-//  * K and V tiles of 64 keys are staged through LDS with register double buffering: the global
-//    loads of tile t+1 are issued before the MFMAs of tile t.  V is transposed on its way into LDS
-//    (V^T rows = value channels) so that the P.V product reads contiguous key runs.
-//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the accumulator
-//    layout then gives each lane one query column and 16 keys per 32-key block, which is exactly
-//    the B-operand layout P^T needs for O^T = V^T P^T once the key order inside the V^T tile is
-//    permuted (bits 2 and 3 of the key index swapped).  No shuffles are needed between the two
-//    products.
-//  * Each branch keeps its own online-softmax state (running max, running sum) per query row in
-//    registers; the lane pair (c, c+32) holding one query column agrees on the max with one
-//    cross-lane exchange.  exp is evaluated as exp2 with log2(e)/sqrt(d) folded into one FMA.
+//  * K and V tiles of 64 keys stream global -> LDS with buffer loads that write LDS directly
+//    (no staging registers); the buffer range check returns zeros past the last row.  Tiles are
+//    double buffered: the loads of tile t+1 are in flight during the MFMAs of tile t.  LDS rows
+//    are dense and XOR-swizzled for the 64-bank (256 B per clock) LDS: 16-byte chunks of K by
+//    (row >> 1) & 7 (128-byte rows) or row & 15 (256-byte rows), 32-byte chunks of V by
+//    2 (row & 3), so the MFMA operand reads are conflict-free (measured with
+//    SQ_LDS_BANK_CONFLICT).  Per-lane read offsets are computed once, outside the key loop.
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16.  Its accumulator
+//    gives each lane one query column and, per 32-key block, keys {8j + 4h + r}; split into two
+//    16-key halves these are exactly the B operand P^T of O^T = V^T P^T.  The matching V^T
+//    operand comes straight from the row-major V tile with ds_read_b64_tr_b16 (a transposing LDS
+//    read: per 16-lane group, each lane receives one column of a 4-key x 16-channel block).
+//  * Each branch keeps its own online-softmax state per query row.  The running max moves only
+//    when a row's new max exceeds it by more than 2^8 in exp2 units (the accumulators are then
+//    rescaled); otherwise the stale max is kept, which changes no result because numerator and
+//    row sum share it.  exp is exp2 with log2(e)/sqrt(d) folded into one FMA; the row sums add
+//    the rounded weights the MFMA consumes (v_dot2 of packed pairs against 1).
 //  * Epilogue: O = acc_1 / l_1 - lambda acc_2 / l_2, V1 RMS norm + scale, bf16 RNE store.
 //  * Causal: tiles past a wavefront's last row are skipped; only tiles crossing the diagonal or
-//    the ragged end are masked element by element.  Row blocks are issued heaviest first and
-//    all blocks of one head land on one XCD when the head count is a multiple of 8.
+//    the ragged end are masked element by element.  Row blocks are issued heaviest first and all
+//    row blocks of one head land on one XCD when the head count is a multiple of 8.
+//  * F16PV (V2): P.V runs on the fp16 MFMA (P and V rounded to fp16, 11 significant bits instead
+//    of bf16's 8).  V is then staged through registers and converted; a V tile holding any
+//    |v| > 65504 stays bf16 and is multiplied on the bf16 MFMA, decided by a workgroup vote.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -36,36 +45,68 @@ constexpr int kBN = 64;     // keys per tile
 constexpr int kDV = 128;    // value width
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for the running max
+constexpr float kLazyLog2 = 8.f;     // largest exp2 argument allowed before the max is moved
+constexpr float kF16Max = 65504.f;   // largest fp16 magnitude
+constexpr int kRsrcWord3 = 0x00020000;  // buffer resource flags word for gfx9-family targets
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int DQK, bool V2>
 struct Cfg {
-  static constexpr int KSTR = DQK + 8;               // LDS row stride (elements) of a K tile
-  static constexpr int VSTR = kBN + 8;               // LDS row stride (elements) of a V^T tile
   static constexpr int NK = V2 ? 1 : 2;              // K tiles per stage (shared K in V2)
-  static constexpr int K_ELEMS = kBN * KSTR;
-  static constexpr int V_ELEMS = kDV * VSTR;
+  static constexpr int K_ELEMS = kBN * DQK;          // one K tile, dense
+  static constexpr int V_ELEMS = kBN * kDV;          // one V tile, dense
   static constexpr int STAGE = NK * K_ELEMS + V_ELEMS;
-  static constexpr int KCH = kBN * DQK / 8 / kThreads;  // 16-byte K chunks per thread per tensor
+  static constexpr int K_LOADS = K_ELEMS * 2 / 1024; // 1 KB wavefront DMA loads per K tile
+  static constexpr int V_LOADS = V_ELEMS * 2 / 1024;
   static constexpr int TQ = DQK / 16;                // MFMA k-steps over the head width
 };
 
-// Position of key `kk` (0..63) inside a V^T tile row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int kk) { return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1); }
-
-__device__ __forceinline__ bf16x8 lds_read8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-
-__device__ __forceinline__ bf16x8 cvt8(const f32x16& s, int base) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (bf16)s[base + i];
-  return r;
+// XOR swizzle of 16-byte chunk indices in a dense K tile row (64 banks of 4 bytes).
+template <int DQK>
+__device__ __forceinline__ int k_swz(int row) {
+  return DQK == 64 ? ((row >> 1) & 7) : (row & 15);
+}
+// Element offset of (row, col) in a dense K tile.
+template <int DQK>
+__device__ __forceinline__ int k_off(int row, int col) {
+  return row * DQK + ((((col >> 3) ^ k_swz<DQK>(row))) << 3) + (col & 7);
+}
+// Element offset of (row, col) in a dense V tile (128 channels) with 32-byte chunks swizzled.
+__device__ __forceinline__ int v_off(int row, int col) {
+  return row * kDV + ((((col >> 4) ^ (2 * (row & 3)))) << 4) + (col & 15);
 }
 
-__device__ __forceinline__ f16x8 cvt8h(const f32x16& s, int base) {
-  f16x8 r;
+// max / sum of x over the lane pair (l, l ^ 32).  (A v_permlane32_swap formulation was tried:
+// the compiler treated both of its results as one value, so the exchange goes through
+// ds_bpermute.)
+__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
+
+// Round 8 consecutive weights of s to a packed MFMA operand and add the rounded values to l
+// (v_dot2 of each packed pair against (1, 1)).  Each pair is converted and summed on its own.
+__device__ __forceinline__ bf16x8 cvt8_sum(const f32x16& s, int base, float& l) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  u32x4 w;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (_Float16)s[base + i];
-  return r;
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 h = {(bf16)s[base + 2 * i], (bf16)s[base + 2 * i + 1]};
+    l = __builtin_amdgcn_fdot2_f32_bf16(h, one, l, false);
+    w[i] = __builtin_bit_cast(uint32_t, h);
+  }
+  return __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ f16x8 cvt8h_sum(const f32x16& s, int base, float& l) {
+  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = {(_Float16)s[base + 2 * i], (_Float16)s[base + 2 * i + 1]};
+    l = __builtin_amdgcn_fdot2(h, one, l, false);
+    w[i] = __builtin_bit_cast(uint32_t, h);
+  }
+  return __builtin_bit_cast(f16x8, w);
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
@@ -73,23 +114,36 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// Largest magnitude an fp16 operand may take without overflowing.
-constexpr float kF16Max = 65504.f;
+// Transposing LDS read (see file header): returns 4 consecutive-row elements of one column.
+__device__ __forceinline__ u32x2 lds_read_tr(const bf16* p) {
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
-// F16PV: the P.V product runs on the fp16 MFMA (P and V rounded to fp16, 11 significant bits,
-// instead of bf16's 8).  A V tile holding any |v| > 65504 is staged and multiplied in bf16
-// instead, decided by a workgroup-wide vote, so no input range is lost.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
 template <int DQK, bool V2, int PPW, bool F16PV>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p) {
   using C = Cfg<DQK, V2>;
   constexpr int WPP = V2 ? 4 / PPW : 4;  // wavefronts per head (pair)
   constexpr int BM = 32 * WPP;           // query rows per workgroup
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * C::STAGE];
   __shared__ int vote[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (scalar)
   const int c = lane & 31;   // query column within the wave's 32 rows
   const int hh = lane >> 5;  // half of the wavefront
   const int rb = p.n_row_blocks - 1 - (int)blockIdx.y;  // heaviest row block first
@@ -117,26 +171,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
   // each head (pair) is owned by exactly one wave group of the b == 0, rb == 0 workgroups
   if (p.lam.out != nullptr && b == 0 && rb == 0 && (w % WPP) == 0 && lane == 0) p.lam.out[qh] = lam;
 
+  // ---- buffer resources over each head slice: rows >= N fall outside and read as zeros
   const bf16* q1 = static_cast<const bf16*>(p.q1) + b * p.sq1.sb + qh * p.sq1.sh;
   const bf16* q2 = static_cast<const bf16*>(p.q2) + b * p.sq2.sb + qh * p.sq2.sh;
-  const bf16* kb1 = static_cast<const bf16*>(p.k1) + b * p.sk1.sb + kvh * p.sk1.sh;
-  const bf16* kb2 = static_cast<const bf16*>(p.k2) + b * p.sk2.sb + kvh * p.sk2.sh;
-  const bf16* vb = static_cast<const bf16*>(p.v) + b * p.sv.sb + kvh * p.sv.sh;
+  const __amdgpu_buffer_rsrc_t rq1 = make_rsrc(q1, (uint32_t)(N * p.sq1.sn * 2));
+  const __amdgpu_buffer_rsrc_t rq2 = make_rsrc(q2, (uint32_t)(N * p.sq2.sn * 2));
+  const uint32_t k1_row = (uint32_t)(p.sk1.sn * 2), k2_row = (uint32_t)(p.sk2.sn * 2);
+  const uint32_t v_row = (uint32_t)(p.sv.sn * 2);
 
   // ---- Q^T B-operands: lane holds query row wrow + c, head-width elements 16t + 8hh .. +7
   bf16x8 qf[2][C::TQ];
   {
-    const int row = wrow + c;
-    const bool ok = row < N;
+    const uint32_t r1 = (uint32_t)((wrow + c) * p.sq1.sn * 2), r2 = (uint32_t)((wrow + c) * p.sq2.sn * 2);
 #pragma unroll
     for (int t = 0; t < C::TQ; ++t) {
-      u32x4 a = {0u, 0u, 0u, 0u}, e = {0u, 0u, 0u, 0u};
-      if (ok) {
-        a = load16(q1 + (int64_t)row * p.sq1.sn + 16 * t + 8 * hh);
-        e = load16(q2 + (int64_t)row * p.sq2.sn + 16 * t + 8 * hh);
-      }
-      qf[0][t] = __builtin_bit_cast(bf16x8, a);
-      qf[1][t] = __builtin_bit_cast(bf16x8, e);
+      qf[0][t] = __builtin_bit_cast(bf16x8, bload16(rq1, r1 + 32 * t + 16 * hh));
+      qf[1][t] = __builtin_bit_cast(bf16x8, bload16(rq2, r2 + 32 * t + 16 * hh));
     }
   }
 
@@ -144,85 +194,87 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
   const int kv_end = p.causal ? min(N, row0 + BM) : N;
   const int ntiles = (kv_end + kBN - 1) / kBN;
 
-  // ---- global -> register staging of one K/V tile
-  u32x4 kreg[C::NK][C::KCH];
-  u32x4 vreg[4];
-  const int v_kq = tid & 15;  // keys 4*v_kq .. +3 of the tile
-  const int v_cc = tid >> 4;  // value channels 8*v_cc .. +7
-
-  auto load_tile = [&](int kt) {
+  // ---- tile loads.  A wavefront DMA load writes 64 x 16 B contiguously at lane order; each
+  // lane fetches the global chunk that belongs at its (swizzled) LDS slot.  The tile's first row
+  // moves into the buffer base (scalar), so the per-lane offsets are loop invariant.
+  constexpr int KPW = C::K_LOADS / 4;  // K DMA loads per wave per tensor
+  constexpr int VPW = C::V_LOADS / 4;
+  uint32_t k_lane[C::NK][KPW], v_lane[VPW];
 #pragma unroll
-    for (int nk = 0; nk < C::NK; ++nk) {
-      const bf16* kb = nk == 0 ? kb1 : kb2;
-      const int64_t sn = nk == 0 ? p.sk1.sn : p.sk2.sn;
+  for (int nk = 0; nk < C::NK; ++nk)
 #pragma unroll
-      for (int s = 0; s < C::KCH; ++s) {
-        const int ch = tid + kThreads * s;
-        const int row = ch / (DQK / 8);
-        const int col = (ch % (DQK / 8)) * 8;
-        const int key = kt + row;
-        kreg[nk][s] = key < N ? load16(kb + (int64_t)key * sn + col) : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < KPW; ++i) {
+      const int e = 512 * (w + 4 * i) + 8 * lane;  // element this lane's 16 B lands on
+      const int row = e / DQK;
+      const int lchunk = ((e % DQK) >> 3) ^ k_swz<DQK>(row);
+      k_lane[nk][i] = (uint32_t)row * (nk == 0 ? k1_row : k2_row) + lchunk * 16;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = kt + 4 * v_kq + r;
-      vreg[r] = key < N ? load16(vb + (int64_t)key * p.sv.sn + 8 * v_cc) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
+  for (int i = 0; i < VPW; ++i) {
+    const int e = 512 * (w + 4 * i) + 8 * lane;
+    const int row = e >> 7;
+    const int slot = (e & 127) >> 3;  // physical 16-byte slot in the row
+    const int lcol = ((((slot >> 1) ^ (2 * (row & 3)))) << 4) + ((slot & 1) << 3);
+    v_lane[i] = (uint32_t)row * v_row + lcol * 2;
+  }
+  const char* k1_base = static_cast<const char*>(p.k1) + 2 * (b * p.sk1.sb + kvh * p.sk1.sh);
+  const char* k2_base = static_cast<const char*>(p.k2) + 2 * (b * p.sk2.sb + kvh * p.sk2.sh);
+  const char* v_base = static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + kvh * p.sv.sh);
 
-  auto store_tile = [&](int buf, bool big) {
+  u32x4 vreg[4];  // F16PV only: V chunks staged through registers
+  auto issue_tile = [&](int kt, int buf) {
     bf16* st = smem + buf * C::STAGE;
+    const int rows_left = N - kt;
 #pragma unroll
     for (int nk = 0; nk < C::NK; ++nk) {
+      const uint32_t krow = nk == 0 ? k1_row : k2_row;
+      const __amdgpu_buffer_rsrc_t rk =
+          make_rsrc((nk == 0 ? k1_base : k2_base) + (size_t)kt * krow, (uint32_t)rows_left * krow);
 #pragma unroll
-      for (int s = 0; s < C::KCH; ++s) {
-        const int ch = tid + kThreads * s;
-        const int row = ch / (DQK / 8);
-        const int col = (ch % (DQK / 8)) * 8;
-        store16(st + nk * C::K_ELEMS + row * C::KSTR + col, kreg[nk][s]);
-      }
+      for (int i = 0; i < KPW; ++i) dma16(rk, st + nk * C::K_ELEMS + 512 * (w + 4 * i), k_lane[nk][i]);
     }
-    // transpose 4 keys x 8 channels into 8 channel rows x 4 keys
     bf16* vt = st + C::NK * C::K_ELEMS;
-    const int pos = vt_pos(4 * v_kq);
+    const __amdgpu_buffer_rsrc_t rvt = make_rsrc(v_base + (size_t)kt * v_row, (uint32_t)rows_left * v_row);
+    if constexpr (!F16PV) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t w0 = vreg[0][m], w1 = vreg[1][m], w2 = vreg[2][m], w3 = vreg[3][m];
-      u32x2 lo, hi;  // channel 2m (low halves) and 2m+1 (high halves)
-      if (F16PV && !big) {
-        lo[0] = pack_h2(bf16_lo(w0), bf16_lo(w1));
-        lo[1] = pack_h2(bf16_lo(w2), bf16_lo(w3));
-        hi[0] = pack_h2(bf16_hi(w0), bf16_hi(w1));
-        hi[1] = pack_h2(bf16_hi(w2), bf16_hi(w3));
-      } else {
-        lo[0] = (w0 & 0xffffu) | (w1 << 16);
-        lo[1] = (w2 & 0xffffu) | (w3 << 16);
-        hi[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-        hi[1] = (w2 >> 16) | (w3 & 0xffff0000u);
+      for (int i = 0; i < VPW; ++i) dma16(rvt, vt + 512 * (w + 4 * i), v_lane[i]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int ch = tid + kThreads * s;  // 16-byte chunk of the 64 x 128 tile
+        vreg[s] = bload16(rvt, (uint32_t)(ch >> 4) * v_row + ((ch & 15) << 4));
       }
-      *reinterpret_cast<u32x2*>(vt + (8 * v_cc + 2 * m) * C::VSTR + pos) = lo;
-      *reinterpret_cast<u32x2*>(vt + (8 * v_cc + 2 * m + 1) * C::VSTR + pos) = hi;
     }
   };
 
-  // Workgroup-wide vote: does the staged V tile hold a value fp16 cannot represent?
-  // (Called by every thread between two barriers; returns the same answer everywhere.)
+  // F16PV: workgroup-wide vote -- does the staged V tile hold a value fp16 cannot represent?
   auto vote_big = [&]() -> bool {
-    if constexpr (!F16PV) {
-      return true;
-    } else {
-      float mx = 0.f;
+    float mx = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(vreg[r][m])), fabsf(bf16_hi(vreg[r][m]))));
-      const bool any = __any(mx > kF16Max);
-      if (lane == 0) vote[w] = any ? 1 : 0;
-      __syncthreads();
-      const bool big = (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
-      return big;
+      for (int m = 0; m < 4; ++m)
+        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(vreg[s][m])), fabsf(bf16_hi(vreg[s][m]))));
+    const bool any = __any(mx > kF16Max);
+    if (lane == 0) vote[w] = any ? 1 : 0;
+    __syncthreads();
+    return (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+  };
+
+  // F16PV: write the staged V chunks (converted to fp16 unless the tile is big) into LDS
+  auto store_v = [&](int buf, bool big) {
+    bf16* vt = smem + buf * C::STAGE + C::NK * C::K_ELEMS;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int ch = tid + kThreads * s;
+      const int row = ch >> 4;
+      const int col = (ch & 15) << 3;
+      u32x4 x = vreg[s];  // 8 channels of one row
+      if (!big) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x[m] = pack_h2(bf16_lo(vreg[s][m]), bf16_hi(vreg[s][m]));
+      }
+      store16(vt + v_off(row, col), x);
     }
   };
 
@@ -239,130 +291,139 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
   const float sl2 = p.scale_log2;
   const bool wave_has_rows = wrow < N;
 
-  auto compute_tile = [&](int buf, int kt, bool big) {
+  // Per-lane LDS read offsets (elements), loop invariant.
+  //  K operand of S^T: row kb*32 + c, chunk 2t + hh; the swizzle depends on the lane only.
+  int k_rd[C::TQ];
+#pragma unroll
+  for (int t = 0; t < C::TQ; ++t) k_rd[t] = k_off<DQK>(c, 16 * t + 8 * hh);
+  //  V^T operand: two transposing reads per operand.  In each 16-lane group lane j addresses row
+  //  key0 + j/4, channels dv0 + 4 (j % 4) .. +3 (see the file header); row & 3 = (j >> 2) & 3,
+  //  so the swizzle again depends on the lane only.
+  int v_rd[4];
+  {
+    const int j = lane & 15, dh = (lane >> 4) & 1;
+    const int row = 4 * hh + (j >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) v_rd[db] = v_off(row, db * 32 + dh * 16 + 4 * (j & 3));
+  }
+
+  // One 32-key half of a tile at a time keeps only 2 x 16 score registers live.
+  auto compute_tile = [&](int buf, int kt, bool bigv) {
     if (!wave_has_rows) return;
-    if (p.causal && kt > wrow + 31) return;  // every key of the tile is in this wave's future
     const bf16* st = smem + buf * C::STAGE;
     const bf16* vt = st + C::NK * C::K_ELEMS;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kh = kt + 32 * kb;             // first key of this half
+      if (p.causal && kh > wrow + 31) break;   // this half and the next are in the future
 
-    // S^T = K Q^T for both branches: s[br][kb] holds keys kb*32 + 8j + 4hh + r (reg 4j + r)
-    f32x16 s[2][2];
+      // S^T = K Q^T for both branches: s[br] holds keys kh + 8j + 4hh + r (reg 4j + r)
+      f32x16 s[2];
 #pragma unroll
-    for (int br = 0; br < 2; ++br) {
-      const bf16* kt_lds = st + (V2 ? 0 : br) * C::K_ELEMS;
+      for (int br = 0; br < 2; ++br)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int r = 0; r < 16; ++r) s[br][r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[br][kb][r] = 0.f;
-#pragma unroll
-        for (int t = 0; t < C::TQ; ++t) {
-          const bf16x8 a = lds_read8(kt_lds + (kb * 32 + c) * C::KSTR + 16 * t + 8 * hh);
-          s[br][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[br][t], s[br][kb], 0, 0, 0);
+      for (int t = 0; t < C::TQ; ++t) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + kb * 32 * DQK + k_rd[t]);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[0][t], s[0], 0, 0, 0);
+        if constexpr (V2) {
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[1][t], s[1], 0, 0, 0);
+        } else {
+          const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + C::K_ELEMS + kb * 32 * DQK + k_rd[t]);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[1][t], s[1], 0, 0, 0);
         }
       }
-    }
 
-    // masking: causal diagonal and ragged end
-    const bool need_mask = (p.causal && kt + kBN - 1 > wrow) || (kt + kBN > N);
-    if (need_mask) {
-      const int qrow = wrow + c;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      // masking: causal diagonal and ragged end
+      if ((p.causal && kh + 31 > wrow) || kh + 32 > N) {
+        const int qrow = wrow + c;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool masked = key >= N || (p.causal && key > qrow);
-          if (masked) {
-            s[0][kb][r] = -INFINITY;
-            s[1][kb][r] = -INFINITY;
+          const int key = kh + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= N || (p.causal && key > qrow)) {
+            s[0][r] = -INFINITY;
+            s[1][r] = -INFINITY;
           }
         }
-    }
+      }
 
-    // online softmax per branch (P is left in s as fp32)
+      // online softmax per branch with a lazily moved max (P is left in s as fp32)
 #pragma unroll
-    for (int br = 0; br < 2; ++br) {
-      float mx = s[br][0][0];
+      for (int br = 0; br < 2; ++br) {
+        float mx = s[br][0];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[br][r]);
+        mx = pair_max(mx);
+        if (__any((mx - mrun[br]) * sl2 > kLazyLog2)) {
+          const float mnew = fmaxf(mrun[br], mx);
+          const float alpha = exp2f((mrun[br] - mnew) * sl2);
+          mrun[br] = mnew;
+          lrun[br] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[br][kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[br], mx);
-      const float alpha = exp2f((mrun[br] - mnew) * sl2);
-      mrun[br] = mnew;
-      const float nm = -mnew * sl2;
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[br][kb][r], sl2, nm));
-          s[br][kb][r] = e;
-          ls += e;
+          for (int db = 0; db < 4; ++db) acc[br][db] *= alpha;
         }
-      lrun[br] = lrun[br] * alpha + ls;
+        const float nm = -mrun[br] * sl2;
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[br][db] *= alpha;
-    }
+        for (int r = 0; r < 16; ++r) s[br][r] = __builtin_amdgcn_exp2f(fmaf(s[br][r], sl2, nm));
+      }
 
-    // O^T += V^T P^T for both branches (the V^T operand is shared)
-    if (F16PV && !big) {
-      f16x8 ph[2][2][2];
+      // O^T += V^T P^T for both branches; the V^T operand (two transposing reads) is shared
 #pragma unroll
-      for (int br = 0; br < 2; ++br)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          ph[br][kb][0] = cvt8h(s[br][kb], 0);
-          ph[br][kb][1] = cvt8h(s[br][kb], 8);
-        }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u) {
+        const int rbase = (kb * 32 + 16 * u) * kDV;  // first row of this 16-key group
+        if (F16PV && !bigv) {
+          const f16x8 p0 = cvt8h_sum(s[0], 8 * u, lrun[0]);
+          const f16x8 p1 = cvt8h_sum(s[1], 8 * u, lrun[1]);
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            const f16x8 a = *reinterpret_cast<const f16x8*>(vt + (db * 32 + c) * C::VSTR + kb * 32 + 16 * u + 8 * hh);
-            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[0][kb][u], acc[0][db], 0, 0, 0);
-            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, ph[1][kb][u], acc[1][db], 0, 0, 0);
+            const u32x2 lo = lds_read_tr(vt + rbase + v_rd[db]);
+            const u32x2 hi = lds_read_tr(vt + rbase + 8 * kDV + v_rd[db]);
+            const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
+            const f16x8 a = __builtin_bit_cast(f16x8, a4);
+            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, p0, acc[0][db], 0, 0, 0);
+            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, p1, acc[1][db], 0, 0, 0);
           }
-    } else {
-      bf16x8 pb[2][2][2];
-#pragma unroll
-      for (int br = 0; br < 2; ++br)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          pb[br][kb][0] = cvt8(s[br][kb], 0);
-          pb[br][kb][1] = cvt8(s[br][kb], 8);
-        }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
+        } else {
+          const bf16x8 p0 = cvt8_sum(s[0], 8 * u, lrun[0]);
+          const bf16x8 p1 = cvt8_sum(s[1], 8 * u, lrun[1]);
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            const bf16x8 a = lds_read8(vt + (db * 32 + c) * C::VSTR + kb * 32 + 16 * u + 8 * hh);
-            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][kb][u], acc[0][db], 0, 0, 0);
-            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][kb][u], acc[1][db], 0, 0, 0);
+            const u32x2 lo = lds_read_tr(vt + rbase + v_rd[db]);
+            const u32x2 hi = lds_read_tr(vt + rbase + 8 * kDV + v_rd[db]);
+            const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
+            const bf16x8 a = __builtin_bit_cast(bf16x8, a4);
+            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p0, acc[0][db], 0, 0, 0);
+            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p1, acc[1][db], 0, 0, 0);
           }
+        }
+      }
     }
   };
 
-  // ---- main loop: one barrier per tile (plus the vote's barrier on the fp16 path)
+  // ---- main loop: DMA of tile t+1 overlaps the MFMAs of tile t; one barrier per tile (plus the
+  // vote's barrier on the F16PV path)
   if (ntiles > 0) {
-    load_tile(0);
-    bool big_cur = vote_big();
-    store_tile(0, big_cur);
+    issue_tile(0, 0);
+    bool big_cur = false;
+    if constexpr (F16PV) {
+      big_cur = vote_big();
+      store_v(0, big_cur);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
       const bool more = it + 1 < ntiles;
-      if (more) load_tile((it + 1) * kBN);
+      if (more) issue_tile((it + 1) * kBN, (it + 1) & 1);
       compute_tile(it & 1, it * kBN, big_cur);
-      if (more) {
-        const bool big_next = vote_big();
-        store_tile((it + 1) & 1, big_next);
-        big_cur = big_next;
+      if constexpr (F16PV) {
+        if (more) {
+          const bool big_next = vote_big();
+          store_v((it + 1) & 1, big_next);
+          big_cur = big_next;
+        }
       }
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
@@ -370,8 +431,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
   // ---- epilogue
   if (!wave_has_rows) return;
   const int qrow = wrow + c;
-  const float l1 = lrun[0] + __shfl_xor(lrun[0], 32);
-  const float l2 = lrun[1] + __shfl_xor(lrun[1], 32);
+  const float l1 = pair_sum(lrun[0]);
+  const float l2 = pair_sum(lrun[1]);
   const float i1 = 1.f / l1;
   const float i2 = lam / l2;
   float o[4][16];
@@ -386,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     }
   float rs = 1.f;
   if (!V2 && p.norm) {
-    ss += __shfl_xor(ss, 32);
+    ss = pair_sum(ss);
     rs = p.out_scale * rsqrtf(ss * (1.f / kDV) + p.eps);
   }
   if (qrow >= N) return;

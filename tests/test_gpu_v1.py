@@ -87,13 +87,24 @@ def test_v1_bf16_full_compare(da, B, H, N, causal):
 
 
 def test_v1_bf16_core_without_norm(da):
-    """flags=DA_V1_NO_NORM exposes (A1 - lambda A2) V; compared after RMS normalisation."""
+    """flags=DA_V1_NO_NORM exposes the core (A1 - lambda A2) V.  Without the V1 norm the core has
+    no fixed scale, so it is checked componentwise against the error bf16 weights can introduce:
+    |err| <= 2^-8 (|A1| |V| + |lambda| |A2| |V| + |ref|) for every element."""
     log("v1 bf16 no-norm N=260")
-    t = wl.make_v1(1, 4, 260, 64, "bf16", seed=3, layers=(2,))
-    got = _run_v1(da, t, "bf16", 2, flags=da.DA_V1_NO_NORM)
-    ref = _oracle_v1(t, "bf16", 2, norm=False)
-    st = compare.bf16_stats(got, ref, normalise=True)
-    assert compare.bf16_ok(st), st
+    layer = 2
+    t = wl.make_v1(1, 4, 260, 64, "bf16", seed=3, layers=(layer,))
+    got = _run_v1(da, t, "bf16", layer, flags=da.DA_V1_NO_NORM)
+    ref = _oracle_v1(t, "bf16", layer, norm=False)
+    lam = oracle_lambda(t["lambda"][layer], layer)
+    worst = 0.0
+    for h in range(4):
+        q1, q2, k1, k2, v = (f64(t[k])[0, h] for k in ("q1", "q2", "k1", "k2", "v"))
+        a1, a2, _ = oracle.diff_maps(q1, k1, q2, k2, lam[h], True)
+        mag = np.abs(a1) @ np.abs(v) + abs(lam[h]) * (np.abs(a2) @ np.abs(v))
+        bound = 2.0 ** -8 * (mag + np.abs(ref[0, h]))
+        worst = max(worst, float(np.max(np.abs(got[0, h] - ref[0, h]) / bound)))
+    log(f"  worst err / bound = {worst:.3f}")
+    assert worst <= 1.0
 
 
 def test_v1_bf16_rows_sum_to_one_minus_lambda(da):
