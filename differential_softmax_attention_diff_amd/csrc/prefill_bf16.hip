@@ -125,8 +125,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// One wavefront-wide 16-byte-per-lane DMA from a buffer into LDS (lane i lands at lds + 16 i).
+// Issued from inline asm so that the compiler does not treat it as aliasing every later LDS read
+// (it would otherwise wait for all outstanding DMA before each one, defeating the prefetch); the
+// kernels order these writes themselves with explicit vmcnt waits and barriers.  M0 holds the LDS
+// base; one wait state separates the M0 write from the DMA.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+  const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void*)lds;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0v), "v"(voff), "s"(r)
+      : "memory");
 }
 
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
@@ -188,6 +200,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
       qf[0][t] = __builtin_bit_cast(bf16x8, bload16(rq1, r1 + 32 * t + 16 * hh));
       qf[1][t] = __builtin_bit_cast(bf16x8, bload16(rq2, r2 + 32 * t + 16 * hh));
     }
+    __builtin_amdgcn_s_waitcnt(0);  // settle Q before the asm tile DMA starts
   }
 
   // ---- key range of this workgroup
@@ -318,6 +331,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
       if (p.causal && kh > wrow + 31) break;   // this half and the next are in the future
 
       // S^T = K Q^T for both branches: s[br] holds keys kh + 8j + 4hh + r (reg 4j + r)
+      __builtin_amdgcn_s_setprio(1);
       f32x16 s[2];
 #pragma unroll
       for (int br = 0; br < 2; ++br)
@@ -335,6 +349,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
         }
       }
 
+      __builtin_amdgcn_s_setprio(0);
       // masking: causal diagonal and ragged end
       if ((p.causal && kh + 31 > wrow) || kh + 32 > N) {
         const int qrow = wrow + c;
@@ -369,6 +384,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
       }
 
       // O^T += V^T P^T for both branches; the V^T operand (two transposing reads) is shared
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int rbase = (kb * 32 + 16 * u) * kDV;  // first row of this 16-key group
@@ -398,6 +414,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
