@@ -114,7 +114,7 @@ def bench_v1(da, torch, steps, warmup):
                      "traffic": measured_traffic("v1_prefill_4k", "prefill"),
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
-                     "kernel": "prefill_kernel<64,false,1,false>"},
+                     "kernel": "prefill_kernel<64,false,false>"},
     }
     return res, (cfg, t)
 
@@ -144,7 +144,7 @@ def bench_v2(da, torch, steps, warmup):
                      "traffic": measured_traffic("v2_prefill_8k", "prefill"),
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
-                     "kernel": "prefill_kernel<128,true,2,true>"},
+                     "kernel": "prefill_kernel<128,true,true>"},
     }
 
 

@@ -35,6 +35,8 @@
 //  * F16PV (V2): P.V runs on the fp16 MFMA (P and V rounded to fp16, 11 significant bits instead
 //    of bf16's 8).  V is then staged through registers and converted; a V tile holding any
 //    |v| > 65504 stays bf16 and is multiplied on the bf16 MFMA, decided by a workgroup vote.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -45,22 +47,12 @@ constexpr int kBN = 64;     // keys per tile
 constexpr int kDV = 128;    // value width
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for the running max
-constexpr float kLazyLog2 = 8.f;     // largest exp2 argument allowed before the max is moved
+constexpr float kCapSum = 4096.f;    // largest lane weight sum per tile (2^12) before the max moves
 constexpr float kF16Max = 65504.f;   // largest fp16 magnitude
 constexpr int kRsrcWord3 = 0x00020000;  // buffer resource flags word for gfx9-family targets
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int DQK, bool V2>
-struct Cfg {
-  static constexpr int NK = V2 ? 1 : 2;              // K tiles per stage (shared K in V2)
-  static constexpr int K_ELEMS = kBN * DQK;          // one K tile, dense
-  static constexpr int V_ELEMS = kBN * kDV;          // one V tile, dense
-  static constexpr int STAGE = NK * K_ELEMS + V_ELEMS;
-  static constexpr int K_LOADS = K_ELEMS * 2 / 1024; // 1 KB wavefront DMA loads per K tile
-  static constexpr int V_LOADS = V_ELEMS * 2 / 1024;
-  static constexpr int TQ = DQK / 16;                // MFMA k-steps over the head width
-};
 
 // XOR swizzle of 16-byte chunk indices in a dense K tile row (64 banks of 4 bytes).
 template <int DQK>
@@ -145,74 +137,103 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
-template <int DQK, bool V2, int PPW, bool F16PV>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p) {
-  using C = Cfg<DQK, V2>;
-  constexpr int WPP = V2 ? 4 / PPW : 4;  // wavefronts per head (pair)
-  constexpr int BM = 32 * WPP;           // query rows per workgroup
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * C::STAGE];
-  __shared__ int vote[4];
+// ------------------------------------------------------------------------------------------------
+constexpr int kSBN = 32;  // keys per tile
+
+template <int DQK, bool V2>
+struct SCfg {
+  static constexpr int NK = V2 ? 1 : 2;                 // K tensors per tile (V2: one shared K)
+  static constexpr int K_ELEMS = kSBN * DQK;            // one K tensor tile
+  static constexpr int KBUF = NK * K_ELEMS;             // one K buffer (all K tensors)
+  static constexpr int VBUF = kSBN * kDV;               // one V buffer
+  static constexpr int K_LOADS = K_ELEMS * 2 / 1024;    // 1 KB wavefront DMA loads per K tile
+  static constexpr int V_LOADS = VBUF * 2 / 1024;
+  static constexpr int TQ = DQK / 16;                   // MFMA k-steps over the head width
+  static constexpr int SMEM = 2 * KBUF + 2 * VBUF;      // [K0 | K1 | V0 | V1]
+};
+
+// 8 packed fp16 values -> 8 packed bf16 values (RNE)
+__device__ __forceinline__ u32x4 f16x8_to_bf16x8(u32x4 x) {
+  const f16x8 h = __builtin_bit_cast(f16x8, x);
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)(float)h[i];
+  return __builtin_bit_cast(u32x4, r);
+}
+
+template <int DQK, bool V2, bool F16PV>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(V2 ? 3 : 4)))
+void prefill_kernel(const PrefillParams p) {
+  using C = SCfg<DQK, V2>;
+  constexpr int BM = 64;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[C::SMEM];
+  __shared__ int vflag[2][4];
+  static_assert(C::SMEM * 2 >= 2 * 64 * 64 * 4, "epilogue exchange must fit the tile buffers");
+  static_assert(C::KBUF == C::VBUF && ((C::KBUF * 2) & (C::KBUF * 2 - 1)) == 0,
+                "buffers flip by XOR of one power of two");
+  constexpr uint32_t kFlip = C::KBUF * 2;  // bytes between the two buffers of K (and of V)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (scalar)
-  const int c = lane & 31;   // query column within the wave's 32 rows
-  const int hh = lane >> 5;  // half of the wavefront
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int br = w >> 1;     // softmax branch of this wave
+  const int rh = w & 1;      // row half
+  const int c = lane & 31;
+  const int hh = lane >> 5;
   const int rb = p.n_row_blocks - 1 - (int)blockIdx.y;  // heaviest row block first
   const int row0 = rb * BM;
+  const int wrow = row0 + 32 * rh;
+  const int N = p.N;
 
   int b, kvh, qh;
-  int wrow;
   if (!V2) {
     b = blockIdx.x / p.heads;
     qh = blockIdx.x % p.heads;
     kvh = qh;
-    wrow = row0 + 32 * w;
   } else {
-    const int grp = blockIdx.x % p.groups_per_kv;
-    const int bg = blockIdx.x / p.groups_per_kv;
-    kvh = bg % p.Hkv;
-    b = bg / p.Hkv;
-    qh = kvh * p.pairs_per_kv + grp * PPW + w / WPP;
-    wrow = row0 + 32 * (w % WPP);
+    // consecutive blocks walk KV heads first, so all pairs of one KV head share an XCD
+    const int bk = p.B * p.Hkv;
+    const int i = blockIdx.x / bk;
+    const int rem = blockIdx.x % bk;
+    b = rem / p.Hkv;
+    kvh = rem % p.Hkv;
+    qh = kvh * p.pairs_per_kv + i;
   }
-  const int N = p.N;
 
-  // ---- lambda prologue (per head / pair)
-  const float lam = head_lambda(p.lam, qh, lane);
-  // each head (pair) is owned by exactly one wave group of the b == 0, rb == 0 workgroups
-  if (p.lam.out != nullptr && b == 0 && rb == 0 && (w % WPP) == 0 && lane == 0) p.lam.out[qh] = lam;
 
-  // ---- buffer resources over each head slice: rows >= N fall outside and read as zeros
-  const bf16* q1 = static_cast<const bf16*>(p.q1) + b * p.sq1.sb + qh * p.sq1.sh;
-  const bf16* q2 = static_cast<const bf16*>(p.q2) + b * p.sq2.sb + qh * p.sq2.sh;
-  const __amdgpu_buffer_rsrc_t rq1 = make_rsrc(q1, (uint32_t)(N * p.sq1.sn * 2));
-  const __amdgpu_buffer_rsrc_t rq2 = make_rsrc(q2, (uint32_t)(N * p.sq2.sn * 2));
-  const uint32_t k1_row = (uint32_t)(p.sk1.sn * 2), k2_row = (uint32_t)(p.sk2.sn * 2);
-  const uint32_t v_row = (uint32_t)(p.sv.sn * 2);
-
-  // ---- Q^T B-operands: lane holds query row wrow + c, head-width elements 16t + 8hh .. +7
-  bf16x8 qf[2][C::TQ];
+  // ---- this wave's Q^T operand (its own branch): lane holds row wrow + c, cols 16t + 8hh .. +7
+  const bf16* qb = br == 0 ? static_cast<const bf16*>(p.q1) + b * p.sq1.sb + qh * p.sq1.sh
+                           : static_cast<const bf16*>(p.q2) + b * p.sq2.sb + qh * p.sq2.sh;
+  const int64_t qsn = br == 0 ? p.sq1.sn : p.sq2.sn;
+  bf16x8 qf[C::TQ];
   {
-    const uint32_t r1 = (uint32_t)((wrow + c) * p.sq1.sn * 2), r2 = (uint32_t)((wrow + c) * p.sq2.sn * 2);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)(N * qsn * 2));
+    const uint32_t r = (uint32_t)((wrow + c) * qsn * 2);
 #pragma unroll
-    for (int t = 0; t < C::TQ; ++t) {
-      qf[0][t] = __builtin_bit_cast(bf16x8, bload16(rq1, r1 + 32 * t + 16 * hh));
-      qf[1][t] = __builtin_bit_cast(bf16x8, bload16(rq2, r2 + 32 * t + 16 * hh));
-    }
+    for (int t = 0; t < C::TQ; ++t) qf[t] = __builtin_bit_cast(bf16x8, bload16(rq, r + 32 * t + 16 * hh));
     __builtin_amdgcn_s_waitcnt(0);  // settle Q before the asm tile DMA starts
   }
 
-  // ---- key range of this workgroup
   const int kv_end = p.causal ? min(N, row0 + BM) : N;
-  const int ntiles = (kv_end + kBN - 1) / kBN;
+  const int ntiles = (kv_end + kSBN - 1) / kSBN;
+  // tiles this wave computes: up to its last visible key
+  const bool wave_has_rows = wrow < N;
+  const int last_key = p.causal ? min(N, wrow + 32) : N;
+  const int nt_wave = wave_has_rows ? min(ntiles, (last_key + kSBN - 1) / kSBN) : 0;
 
-  // ---- tile loads.  A wavefront DMA load writes 64 x 16 B contiguously at lane order; each
-  // lane fetches the global chunk that belongs at its (swizzled) LDS slot.  The tile's first row
-  // moves into the buffer base (scalar), so the per-lane offsets are loop invariant.
-  constexpr int KPW = C::K_LOADS / 4;  // K DMA loads per wave per tensor
-  constexpr int VPW = C::V_LOADS / 4;
-  uint32_t k_lane[C::NK][KPW], v_lane[VPW];
+  const uint32_t k1_row = (uint32_t)(p.sk1.sn * 2), k2_row = (uint32_t)(p.sk2.sn * 2);
+  const uint32_t v_row = (uint32_t)(p.sv.sn * 2);
+  const char* k1_base = static_cast<const char*>(p.k1) + 2 * (b * p.sk1.sb + kvh * p.sk1.sh);
+  const char* k2_base = static_cast<const char*>(p.k2) + 2 * (b * p.sk2.sb + kvh * p.sk2.sh);
+  const char* v_base = static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + kvh * p.sv.sh);
+
+  // ---- tile loads.  Wave w issues the 1 KB DMA loads j = w + 4i of a K buffer (K1 then K2 in
+  // V1) and of a V buffer (unless V is staged through registers).  Lane offsets are relative to
+  // the tile's first row, which moves into the scalar buffer base.
+  constexpr int KPW = C::K_LOADS / 4;              // per wave per K tensor
+  constexpr int VPW = F16PV ? 0 : C::V_LOADS / 4;  // per wave, V
+  uint32_t k_lane[C::NK][KPW];
+  uint32_t v_lane[VPW > 0 ? VPW : 1];
 #pragma unroll
   for (int nk = 0; nk < C::NK; ++nk)
 #pragma unroll
@@ -230,13 +251,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     const int lcol = ((((slot >> 1) ^ (2 * (row & 3)))) << 4) + ((slot & 1) << 3);
     v_lane[i] = (uint32_t)row * v_row + lcol * 2;
   }
-  const char* k1_base = static_cast<const char*>(p.k1) + 2 * (b * p.sk1.sb + kvh * p.sk1.sh);
-  const char* k2_base = static_cast<const char*>(p.k2) + 2 * (b * p.sk2.sb + kvh * p.sk2.sh);
-  const char* v_base = static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + kvh * p.sv.sh);
+  // F16PV staging region of this wave: rows 16 (w >> 1) + q / 8, channels 64 (w & 1) + 8 (q % 8)
+  // for q = lane + 64 s.
+  int vs_row[2], vs_col[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int q = lane + 64 * s;
+    vs_row[s] = 16 * (w >> 1) + (q >> 3);
+    vs_col[s] = 64 * (w & 1) + 8 * (q & 7);
+  }
+  u32x4 vreg[2];
 
-  u32x4 vreg[4];  // F16PV only: V chunks staged through registers
-  auto issue_tile = [&](int kt, int buf) {
-    bf16* st = smem + buf * C::STAGE;
+  auto issue_k = [&](int kt, int buf) {
+    bf16* kb = smem + buf * C::KBUF;
     const int rows_left = N - kt;
 #pragma unroll
     for (int nk = 0; nk < C::NK; ++nk) {
@@ -244,221 +271,244 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
       const __amdgpu_buffer_rsrc_t rk =
           make_rsrc((nk == 0 ? k1_base : k2_base) + (size_t)kt * krow, (uint32_t)rows_left * krow);
 #pragma unroll
-      for (int i = 0; i < KPW; ++i) dma16(rk, st + nk * C::K_ELEMS + 512 * (w + 4 * i), k_lane[nk][i]);
-    }
-    bf16* vt = st + C::NK * C::K_ELEMS;
-    const __amdgpu_buffer_rsrc_t rvt = make_rsrc(v_base + (size_t)kt * v_row, (uint32_t)rows_left * v_row);
-    if constexpr (!F16PV) {
-#pragma unroll
-      for (int i = 0; i < VPW; ++i) dma16(rvt, vt + 512 * (w + 4 * i), v_lane[i]);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int ch = tid + kThreads * s;  // 16-byte chunk of the 64 x 128 tile
-        vreg[s] = bload16(rvt, (uint32_t)(ch >> 4) * v_row + ((ch & 15) << 4));
-      }
+      for (int i = 0; i < KPW; ++i) dma16(rk, kb + nk * C::K_ELEMS + 512 * (w + 4 * i), k_lane[nk][i]);
     }
   };
-
-  // F16PV: workgroup-wide vote -- does the staged V tile hold a value fp16 cannot represent?
-  auto vote_big = [&]() -> bool {
+  auto issue_v = [&](int kt, int buf) {
+    const int rows_left = N - kt;
+    const __amdgpu_buffer_rsrc_t rvt = make_rsrc(v_base + (size_t)kt * v_row, (uint32_t)rows_left * v_row);
+    if constexpr (!F16PV) {
+      bf16* vb = smem + 2 * C::KBUF + buf * C::VBUF;
+#pragma unroll
+      for (int i = 0; i < VPW; ++i) dma16(rvt, vb + 512 * (w + 4 * i), v_lane[i]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) vreg[s] = bload16(rvt, (uint32_t)vs_row[s] * v_row + vs_col[s] * 2);
+    }
+  };
+  // F16PV: convert the staged region (unless it holds a value fp16 cannot represent), store it,
+  // and publish the region's format
+  auto finish_v = [&](int buf) {
+    bf16* vb = smem + 2 * C::KBUF + buf * C::VBUF;
     float mx = 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(vreg[s][m])), fabsf(bf16_hi(vreg[s][m]))));
-    const bool any = __any(mx > kF16Max);
-    if (lane == 0) vote[w] = any ? 1 : 0;
-    __syncthreads();
-    return (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
-  };
-
-  // F16PV: write the staged V chunks (converted to fp16 unless the tile is big) into LDS
-  auto store_v = [&](int buf, bool big) {
-    bf16* vt = smem + buf * C::STAGE + C::NK * C::K_ELEMS;
+    const bool big = __any(mx > kF16Max);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ch = tid + kThreads * s;
-      const int row = ch >> 4;
-      const int col = (ch & 15) << 3;
-      u32x4 x = vreg[s];  // 8 channels of one row
+    for (int s = 0; s < 2; ++s) {
+      u32x4 x = vreg[s];
       if (!big) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) x[m] = pack_h2(bf16_lo(vreg[s][m]), bf16_hi(vreg[s][m]));
       }
-      store16(vt + v_off(row, col), x);
+      store16(vb + v_off(vs_row[s], vs_col[s]), x);
     }
+    if (lane == 0) vflag[buf][w] = big ? 1 : 0;
+  };
+  auto issue_tile = [&](int i) {
+    issue_k(i * kSBN, i & 1);
+    issue_v(i * kSBN, i & 1);
   };
 
-  // ---- per-wave running state
-  f32x16 acc[2][4];
+  f32x16 acc[4];
 #pragma unroll
-  for (int br = 0; br < 2; ++br)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[br][db][r] = 0.f;
-  float mrun[2] = {kNegBig, kNegBig};
-  float lrun[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float mrun = kNegBig, lrun = 0.f;
   const float sl2 = p.scale_log2;
-  const bool wave_has_rows = wrow < N;
 
-  // Per-lane LDS read offsets (elements), loop invariant.
-  //  K operand of S^T: row kb*32 + c, chunk 2t + hh; the swizzle depends on the lane only.
-  int k_rd[C::TQ];
-#pragma unroll
-  for (int t = 0; t < C::TQ; ++t) k_rd[t] = k_off<DQK>(c, 16 * t + 8 * hh);
-  //  V^T operand: two transposing reads per operand.  In each 16-lane group lane j addresses row
-  //  key0 + j/4, channels dv0 + 4 (j % 4) .. +3 (see the file header); row & 3 = (j >> 2) & 3,
-  //  so the swizzle again depends on the lane only.
-  int v_rd[4];
+  // Per-lane LDS byte addresses of the MFMA operands, one register each; they flip to the other
+  // buffer after use (one XOR).  Both swizzles act on address bits that the operand index only
+  // XORs into, so operand t (or db) sits at base ^ (constant * t):
+  //  K operand t of S^T: row c, 16-byte chunk (2t + hh) ^ swz(c), i.e. k_ad ^ 32 t.
+  //  V^T operand db: two transposing reads; in each 16-lane group lane j addresses row
+  //  4 hh + j / 4 (plus 16 u, and 8 for the upper read), channels 32 db + 16 dh + 4 (j % 4),
+  //  whose 32-byte chunk db ^ (row & 3) puts it at v_ad ^ 64 db.
+  uint32_t k_ad = 2u * ((V2 ? 0 : br * C::K_ELEMS) + k_off<DQK>(c, 8 * hh));
+  uint32_t v_ad;
   {
     const int j = lane & 15, dh = (lane >> 4) & 1;
     const int row = 4 * hh + (j >> 2);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) v_rd[db] = v_off(row, db * 32 + dh * 16 + 4 * (j & 3));
+    v_ad = 2u * (2 * C::KBUF + v_off(row, dh * 16 + 4 * (j & 3)));
   }
+  const char* sb = reinterpret_cast<const char*>(smem);
+  // max over the lane pair (l, l ^ 32) through ds_bpermute with a loop-invariant address
+  const int bp_pair = (lane ^ 32) << 2;
+  auto pmax = [&](float x) {
+    return fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(bp_pair, __builtin_bit_cast(int, x))));
+  };
 
-  // One 32-key half of a tile at a time keeps only 2 x 16 score registers live.
-  auto compute_tile = [&](int buf, int kt, bool bigv) {
-    if (!wave_has_rows) return;
-    const bf16* st = smem + buf * C::STAGE;
-    const bf16* vt = st + C::NK * C::K_ELEMS;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kh = kt + 32 * kb;             // first key of this half
-      if (p.causal && kh > wrow + 31) break;   // this half and the next are in the future
+  // K operand t of the next score tile; V^T operand db, lower or upper read, 16-key group u
+  auto k_operand = [&](int t) { return *reinterpret_cast<const bf16x8*>(sb + (k_ad ^ (32u * t))); };
+  auto v_read = [&](int db, int u, int upper) {
+    return lds_read_tr(reinterpret_cast<const bf16*>(sb + (v_ad ^ (64u * db))) + (16 * u + 8 * upper) * kDV);
+  };
 
-      // S^T = K Q^T for both branches: s[br] holds keys kh + 8j + 4hh + r (reg 4j + r)
-      __builtin_amdgcn_s_setprio(1);
-      f32x16 s[2];
+  auto scores = [&]() {
+    f32x16 s;
 #pragma unroll
-      for (int br = 0; br < 2; ++br)
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[br][r] = 0.f;
+    for (int t = 0; t < C::TQ; ++t) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(t), qf[t], s, 0, 0, 0);
+    return s;
+  };
+  // causal diagonal and ragged end only
+  auto mask = [&](f32x16& s, int kt) {
+    if ((p.causal && kt + 31 > wrow) || kt + kSBN > N) {
+      const int qrow = wrow + c;
 #pragma unroll
-      for (int t = 0; t < C::TQ; ++t) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(st + kb * 32 * DQK + k_rd[t]);
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[0][t], s[0], 0, 0, 0);
-        if constexpr (V2) {
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[1][t], s[1], 0, 0, 0);
-        } else {
-          const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(st + C::K_ELEMS + kb * 32 * DQK + k_rd[t]);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[1][t], s[1], 0, 0, 0);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key >= N || (p.causal && key > qrow)) s[r] = -INFINITY;
       }
-
-      __builtin_amdgcn_s_setprio(0);
-      // masking: causal diagonal and ragged end
-      if ((p.causal && kh + 31 > wrow) || kh + 32 > N) {
-        const int qrow = wrow + c;
+    }
+  };
+  // weights exp2((s - m) log2(e) / sqrt(d)) for the reference max m, rounded to the two packed
+  // P operands (16 keys each); tl gets the lane's sum of the rounded weights
+  using POp = std::conditional_t<F16PV, f16x8, bf16x8>;
+  auto weights = [&](const f32x16& s, POp& p0, POp& p1, float& tl, auto half_tag) {
+    constexpr bool kHalf = decltype(half_tag)::value;
+    const float nm = -mrun * sl2;
+    f32x16 e;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kh + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= N || (p.causal && key > qrow)) {
-            s[0][r] = -INFINITY;
-            s[1][r] = -INFINITY;
-          }
-        }
-      }
-
-      // online softmax per branch with a lazily moved max (P is left in s as fp32)
-#pragma unroll
-      for (int br = 0; br < 2; ++br) {
-        float mx = s[br][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[br][r]);
-        mx = pair_max(mx);
-        if (__any((mx - mrun[br]) * sl2 > kLazyLog2)) {
-          const float mnew = fmaxf(mrun[br], mx);
-          const float alpha = exp2f((mrun[br] - mnew) * sl2);
-          mrun[br] = mnew;
-          lrun[br] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 4; ++db) acc[br][db] *= alpha;
-        }
-        const float nm = -mrun[br] * sl2;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[br][r] = __builtin_amdgcn_exp2f(fmaf(s[br][r], sl2, nm));
-      }
-
-      // O^T += V^T P^T for both branches; the V^T operand (two transposing reads) is shared
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int rbase = (kb * 32 + 16 * u) * kDV;  // first row of this 16-key group
-        if (F16PV && !bigv) {
-          const f16x8 p0 = cvt8h_sum(s[0], 8 * u, lrun[0]);
-          const f16x8 p1 = cvt8h_sum(s[1], 8 * u, lrun[1]);
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const u32x2 lo = lds_read_tr(vt + rbase + v_rd[db]);
-            const u32x2 hi = lds_read_tr(vt + rbase + 8 * kDV + v_rd[db]);
-            const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
-            const f16x8 a = __builtin_bit_cast(f16x8, a4);
-            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, p0, acc[0][db], 0, 0, 0);
-            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, p1, acc[1][db], 0, 0, 0);
-          }
-        } else {
-          const bf16x8 p0 = cvt8_sum(s[0], 8 * u, lrun[0]);
-          const bf16x8 p1 = cvt8_sum(s[1], 8 * u, lrun[1]);
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const u32x2 lo = lds_read_tr(vt + rbase + v_rd[db]);
-            const u32x2 hi = lds_read_tr(vt + rbase + 8 * kDV + v_rd[db]);
-            const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
-            const bf16x8 a = __builtin_bit_cast(bf16x8, a4);
-            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p0, acc[0][db], 0, 0, 0);
-            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p1, acc[1][db], 0, 0, 0);
-          }
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nm));
+    tl = 0.f;
+    if constexpr (kHalf) {
+      p0 = __builtin_bit_cast(POp, cvt8h_sum(e, 0, tl));
+      p1 = __builtin_bit_cast(POp, cvt8h_sum(e, 8, tl));
+    } else {
+      p0 = __builtin_bit_cast(POp, cvt8_sum(e, 0, tl));
+      p1 = __builtin_bit_cast(POp, cvt8_sum(e, 8, tl));
     }
   };
 
-  // ---- main loop: DMA of tile t+1 overlaps the MFMAs of tile t; one barrier per tile (plus the
-  // vote's barrier on the F16PV path)
-  if (ntiles > 0) {
-    issue_tile(0, 0);
-    bool big_cur = false;
+  // One tile of this wave's branch.  The softmax keeps a reference max m per row that moves only
+  // when needed: the weights of a tile are formed against the current m, and only if some lane's
+  // weight sum exceeds 2^kCap (a score beyond m + kCap in exp2 units, or the very first tile,
+  // whose m is still -1e30) does the tile's exact row max get taken, the accumulators rescaled and
+  // the weights formed again.  Every weight the MFMA sees is then at most 2^kCap, so fp16 P
+  // cannot overflow.  softmax(s) does not depend on m, so the result is the same as with an exact
+  // running max.
+  auto compute_tile = [&](int i, auto slow_tag) {
+    constexpr bool kSlow = decltype(slow_tag)::value;
+    constexpr bool kHalf = F16PV && !kSlow;
+    const int kt = i * kSBN;
+    __builtin_amdgcn_s_setprio(1);
+    f32x16 s = scores();
+    __builtin_amdgcn_s_setprio(0);
+    mask(s, kt);
+    POp p0, p1;
+    float tl;
+    weights(s, p0, p1, tl, std::integral_constant<bool, kHalf>{});
+    if (__any(!(tl <= kCapSum))) {
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = pmax(mx);
+      const float mnew = fmaxf(mrun, mx);
+      const float alpha = exp2f((mrun - mnew) * sl2);
+      mrun = mnew;
+      lrun *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+      weights(s, p0, p1, tl, std::integral_constant<bool, kHalf>{});
+    }
+    lrun += tl;
+
+    // O^T += V^T P^T, 16 keys per MFMA
+    const int vbuf = i & 1;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const POp pp = u == 0 ? p0 : p1;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const u32x2 lo = v_read(db, u, 0);
+        const u32x2 hi = v_read(db, u, 1);
+        u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
+        if constexpr (kHalf) {
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a4), pp, acc[db], 0, 0, 0);
+        } else {
+          // bf16 P.V; on the F16PV slow path the fp16 regions are widened back to bf16 (exact for
+          // every value fp16 holds with 8 or more significant bits)
+          if constexpr (kSlow) {
+            if (!vflag[vbuf][2 * u + (db >> 1)]) a4 = f16x8_to_bf16x8(a4);
+          }
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
+                                                           __builtin_bit_cast(bf16x8, pp), acc[db], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    k_ad ^= kFlip;
+    v_ad ^= kFlip;
+  };
+
+  // ---- main loop: loads of tile t+1 are in flight during the MFMAs of tile t.  A wave computes
+  // the tiles up to its last visible key, then only helps load and meets the barriers, so that
+  // the loop that carries the accumulators has no path around them.  F16PV: from the first tile
+  // with a bf16 region on, a wave stays on the bf16 path, in a loop of its own so that the
+  // accumulators never merge from two paths inside one loop.
+  auto tile_big = [&](int i) {
+    const int vb = i & 1;
+    return F16PV && (vflag[vb][0] | vflag[vb][1] | vflag[vb][2] | vflag[vb][3]) != 0;
+  };
+  auto step = [&](int i, auto slow_tag) {
+    const bool more = i + 1 < ntiles;
+    if (more) issue_tile(i + 1);
+    compute_tile(i, slow_tag);
     if constexpr (F16PV) {
-      big_cur = vote_big();
-      store_v(0, big_cur);
+      if (more) finish_v((i + 1) & 1);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      const bool more = it + 1 < ntiles;
-      if (more) issue_tile((it + 1) * kBN, (it + 1) & 1);
-      compute_tile(it & 1, it * kBN, big_cur);
-      if constexpr (F16PV) {
-        if (more) {
-          const bool big_next = vote_big();
-          store_v((it + 1) & 1, big_next);
-          big_cur = big_next;
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+  };
+  issue_tile(0);
+  if constexpr (F16PV) finish_v(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int it = 0;
+  for (; it < nt_wave; ++it) {
+    if (tile_big(it)) break;
+    step(it, std::false_type{});
+  }
+  if constexpr (F16PV) {
+    for (; it < nt_wave; ++it) step(it, std::true_type{});
+  }
+  for (; it < ntiles; ++it) {
+    if (it + 1 < ntiles) {
+      issue_tile(it + 1);
+      if constexpr (F16PV) finish_v((it + 1) & 1);
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
-  // ---- epilogue
-  if (!wave_has_rows) return;
-  const int qrow = wrow + c;
-  const float l1 = pair_sum(lrun[0]);
-  const float l2 = pair_sum(lrun[1]);
-  const float i1 = 1.f / l1;
-  const float i2 = lam / l2;
+  // ---- epilogue: branch-2 waves publish lambda acc_2 / l_2; branch-1 waves finish the rows
+  const float lam = head_lambda(p.lam, qh, lane);
+  if (p.lam.out != nullptr && b == 0 && rb == 0 && w == 0 && lane == 0) p.lam.out[qh] = lam;
+  float* xb = reinterpret_cast<float*>(smem) + rh * (64 * 64);
+  if (br == 1 && wave_has_rows) {
+    const float i2 = lam / pair_sum(lrun);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xb[(db * 16 + r) * 64 + lane] = acc[db][r] * i2;
+  }
+  __syncthreads();
+  if (br == 1 || !wave_has_rows) return;
+  const float i1 = 1.f / pair_sum(lrun);
   float o[4][16];
   float ss = 0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float x = acc[0][db][r] * i1 - acc[1][db][r] * i2;
+      const float x = acc[db][r] * i1 - xb[(db * 16 + r) * 64 + lane];
       o[db][r] = x;
       ss = fmaf(x, x, ss);
     }
@@ -467,6 +517,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
     ss = pair_sum(ss);
     rs = p.out_scale * rsqrtf(ss * (1.f / kDV) + p.eps);
   }
+  const int qrow = wrow + c;
   if (qrow >= N) return;
   bf16* orow = static_cast<bf16*>(p.out) + b * p.so.sb + qh * p.so.sh + (int64_t)qrow * p.so.sn;
 #pragma unroll
@@ -484,26 +535,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillParams p
 
 hipError_t launch_v1_bf16(const PrefillParams& p, hipStream_t stream) {
   PrefillParams q = p;
-  q.n_row_blocks = (p.N + 127) / 128;
+  q.n_row_blocks = (p.N + 63) / 64;
   const dim3 grid(p.B * p.heads, q.n_row_blocks);
-  hipLaunchKernelGGL((prefill_kernel<64, false, 1, false>), grid, dim3(kThreads), 0, stream, q);
+  hipLaunchKernelGGL((prefill_kernel<64, false, false>), grid, dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 
-hipError_t launch_v2_bf16(const PrefillParams& p, int pairs_per_wg, hipStream_t stream) {
+hipError_t launch_v2_bf16(const PrefillParams& p, int /*pairs_per_wg*/, hipStream_t stream) {
   PrefillParams q = p;
   q.pairs_per_kv = p.heads / p.Hkv;
-  if (pairs_per_wg == 2) {
-    q.groups_per_kv = q.pairs_per_kv / 2;
-    q.n_row_blocks = (p.N + 63) / 64;
-    const dim3 grid(p.B * p.Hkv * q.groups_per_kv, q.n_row_blocks);
-    hipLaunchKernelGGL((prefill_kernel<128, true, 2, true>), grid, dim3(kThreads), 0, stream, q);
-  } else {
-    q.groups_per_kv = q.pairs_per_kv;
-    q.n_row_blocks = (p.N + 127) / 128;
-    const dim3 grid(p.B * p.Hkv * q.groups_per_kv, q.n_row_blocks);
-    hipLaunchKernelGGL((prefill_kernel<128, true, 1, true>), grid, dim3(kThreads), 0, stream, q);
-  }
+  q.groups_per_kv = q.pairs_per_kv;
+  q.n_row_blocks = (p.N + 63) / 64;
+  const dim3 grid(p.B * p.heads, q.n_row_blocks);
+  hipLaunchKernelGGL((prefill_kernel<128, true, true>), grid, dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 
