@@ -42,6 +42,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "prefill_bf16.hip"),
     "decode": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "decode_v2.hip"),
+    "decode_v1": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "decode_v1.hip"),
 }
 
 
@@ -176,6 +177,34 @@ def bench_decode(da, torch, steps, warmup):
     }
 
 
+def bench_decode_v1(da, torch, steps, warmup):
+    cfg, t = wl.make("v1_decode_32k")
+    layer = cfg["layers"][0]
+    B, H, L, d = cfg["B"], cfg["H"], cfg["L"], cfg["d"]
+    q1, q2 = to_dev(t["q1"], torch), to_dev(t["q2"], torch)
+    k1, k2, vc = (to_dev(t[k], torch) for k in ("k1cache", "k2cache", "vcache"))
+    del t["k1cache"], t["k2cache"], t["vcache"]
+    lv = [torch.from_numpy(x).to("cuda") for x in t["lambda"][layer]]
+    out = torch.empty((B, H, 2 * d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(da.diffattn_decode_v1_workspace_bytes(B, H, L, d), dtype=torch.uint8,
+                     device="cuda")
+    fn = lambda: da.diffattn_decode_v1(q1, q2, k1, k2, vc, *lv, layer=layer, out=out, workspace=ws)
+    ms = time_launches(fn, steps, warmup, torch)
+    # K1 + K2 + V read once, the two query halves read, the output written
+    nbytes = B * H * L * (d + d + 2 * d) * 2 + 2 * B * H * d * 2 + B * H * 2 * d * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": "v1_decode_32k", "ms": ms, "value": round(gbs, 1), "unit": "GB/s",
+        "config": {"workload": "v1_decode_32k", "B": B, "H": H, "L": L, "d": d, "dv": 2 * d,
+                   "layer": layer, "dtype": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("v1_decode_32k", "decode_v1"),
+                     "algorithmic_bytes": nbytes,
+                     "kernel": "decode_v1_partial_kernel + decode_v1_combine_kernel (whole step)"},
+    }
+
+
 # ------------------------------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the V1 workload)
 # ------------------------------------------------------------------------------------------------
@@ -221,8 +250,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["v1", "v2", "decode"], default=None)
+    ap.add_argument("--warmup", type=int, default=100)  # clocks settle after ~20-50 ms of load
+    ap.add_argument("--only", choices=["v1", "v2", "decode", "decode_v1"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -260,6 +289,10 @@ def main():
     if a.only in (None, "decode"):
         print("[bench] v2 decode", file=sys.stderr, flush=True)
         secondary.append(bench_decode(da, torch, a.steps, a.warmup))
+        torch.cuda.empty_cache()
+    if a.only in (None, "decode_v1"):
+        print("[bench] v1 decode", file=sys.stderr, flush=True)
+        secondary.append(bench_decode_v1(da, torch, a.steps, a.warmup))
         torch.cuda.empty_cache()
     if a.only == "v1" or a.only is None:
         print("[bench] v1 prefill", file=sys.stderr, flush=True)

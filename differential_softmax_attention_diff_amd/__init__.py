@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
   diffattn_fwd_v2(q1, q2, k, v, lq1, lk1, lq2, lk2, layer, ...)        V2 prefill (GQA pairs)
   diffattn_decode(q1, q2, kcache, vcache, lq1, lk1, lq2, lk2, layer, ...)  V2 decode step
   diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits=0)
+  diffattn_decode_v1(q1, q2, k1cache, k2cache, vcache, lq1, lk1, lq2, lk2, layer, ...)  V1 decode
+  diffattn_decode_v1_workspace_bytes(B, H, L, d, num_splits=0)
   diffattn_lambda_init(layer)
 """
 
@@ -23,8 +25,8 @@ import os
 __all__ = [
     "DiffAttnError", "load_library", "LIB_PATH",
     "DA_F32", "DA_BF16", "DA_V1_NO_NORM",
-    "diffattn_fwd_v1", "diffattn_fwd_v2", "diffattn_decode",
-    "diffattn_decode_workspace_bytes", "diffattn_lambda_init",
+    "diffattn_fwd_v1", "diffattn_fwd_v2", "diffattn_decode", "diffattn_decode_v1",
+    "diffattn_decode_workspace_bytes", "diffattn_decode_v1_workspace_bytes", "diffattn_lambda_init",
     "diffattn_status_string", "diffattn_version",
 ]
 
@@ -78,6 +80,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.diffattn_decode_workspace_bytes.restype = sz
     lib.diffattn_decode.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp, sz, vp]
     lib.diffattn_decode.restype = i32
+    lib.diffattn_decode_v1_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.diffattn_decode_v1_workspace_bytes.restype = sz
+    lib.diffattn_decode_v1.argtypes = [T, T, T, T, T, T, i32, i32, i32, i32, i32, L, f32, u32, i32,
+                                       vp, sz, vp]
+    lib.diffattn_decode_v1.restype = i32
     lib.diffattn_lambda_init.argtypes = [i32]
     lib.diffattn_lambda_init.restype = ctypes.c_double
     lib.diffattn_status_string.argtypes = [i32]
@@ -103,6 +110,10 @@ def diffattn_lambda_init(layer: int) -> float:
 
 def diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits: int = 0) -> int:
     return int(load_library().diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits))
+
+
+def diffattn_decode_v1_workspace_bytes(B, H, L, d, num_splits: int = 0) -> int:
+    return int(load_library().diffattn_decode_v1_workspace_bytes(B, H, L, d, num_splits))
 
 
 # ------------------------------------------------------------------------------------------------
@@ -263,4 +274,42 @@ def diffattn_decode(q1, q2, kcache, vcache, lq1=None, lk1=None, lq2=None, lk2=No
         _check(load_library().diffattn_decode(*descs, B, P, Hkv, L, D, dt, ctypes.byref(lam),
                                               int(num_splits), workspace.data_ptr(), ws_bytes, st),
                "diffattn_decode")
+    return out
+
+
+def diffattn_decode_v1(q1, q2, k1cache, k2cache, vcache, lq1=None, lk1=None, lq2=None, lk2=None,
+                       layer=1, *, out=None, eps=1e-5, flags=0, num_splits=0, workspace=None,
+                       lambda_override=None, lambda_out=None, stream=None):
+    """One V1 decode step; q1, q2 [B, H, d], k1cache, k2cache [B, H, L, d], vcache [B, H, L, 2d]
+    -> out [B, H, 2d] (RMS-normalised and scaled by 1 - lambda_init unless DA_V1_NO_NORM).
+
+    ``workspace`` is a GPU byte tensor of at least ``diffattn_decode_v1_workspace_bytes`` bytes;
+    one is allocated when omitted.
+    """
+    torch = _torch()
+    B, H, d = q1.shape
+    L = k1cache.shape[2]
+    if out is None:
+        out = torch.empty((B, H, vcache.shape[-1]), dtype=q1.dtype, device=q1.device)
+    dt = _dtype_code(q1)
+    for nm, t in (("q2", q2), ("k1cache", k1cache), ("k2cache", k2cache), ("vcache", vcache),
+                  ("out", out)):
+        if t.dtype != q1.dtype:
+            raise TypeError(f"{nm} dtype {t.dtype} differs from q1 dtype {q1.dtype}")
+    descs = [_desc(q1, "q1", (B, H, d)), _desc(q2, "q2", (B, H, d)),
+             _desc(k1cache, "k1cache", (B, H, L, d)), _desc(k2cache, "k2cache", (B, H, L, d)),
+             _desc(vcache, "vcache", (B, H, L, 2 * d)), _desc(out, "out", (B, H, 2 * d))]
+    need = diffattn_decode_v1_workspace_bytes(B, H, L, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lam = _lambda(lq1, lk1, lq2, lk2, layer, H, lambda_override, lambda_out, q1.device)
+    with torch.cuda.device(q1.device):
+        st = _stream(q1.device, stream)
+        _check(load_library().diffattn_decode_v1(*descs, B, H, L, d, dt, ctypes.byref(lam),
+                                                 float(eps), int(flags), int(num_splits),
+                                                 workspace.data_ptr(), ws_bytes, st),
+               "diffattn_decode_v1")
     return out

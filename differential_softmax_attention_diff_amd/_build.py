@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libdiffattn.so")
 
-SOURCES = ["abi.cpp", "fwd_v1_f32.hip", "prefill_bf16.hip", "decode_v2.hip"]
+SOURCES = ["abi.cpp", "fwd_v1_f32.hip", "prefill_bf16.hip", "decode_v2.hip", "decode_v1.hip"]
 # Per-source extra flags.  The prefill kernels keep their MFMA accumulators in VGPRs: the online
 # softmax rescales them with vector ALU ops, and AGPR-resident accumulators cost a copy per use.
 # They also never produce a NaN of their own (masked scores are -inf, exp2(-inf) = 0), so the

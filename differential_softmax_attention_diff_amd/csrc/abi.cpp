@@ -109,7 +109,7 @@ da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2
   if (d != 64) return d <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
   if (!(eps >= 0.f) || !std::isfinite(eps)) return DA_ERR_SHAPE;
   if ((flags & ~DA_V1_NO_NORM) != 0u) return DA_ERR_UNSUPPORTED;
-  if ((int64_t)B * H > kMaxGridY || (N + 63) / 64 > kMaxGridY) return DA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > (int64_t)INT32_MAX || (N + 63) / 64 > kMaxGridY) return DA_ERR_UNSUPPORTED;
   const int eb = dtype == DA_F32 ? 4 : 2;
   for (const da_tensor* t : {&q1, &q2, &k1, &k2, &v, &out}) {
     const da_status s = check_tensor(*t, eb);
@@ -146,8 +146,7 @@ da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, 
   if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
   if (D != 128) return D <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
   if (P % Hkv != 0) return DA_ERR_SHAPE;
-  const int ppk = P / Hkv;
-  if (ppk > 8 || (N + 63) / 64 > kMaxGridY) return DA_ERR_UNSUPPORTED;
+  if ((int64_t)B * P > (int64_t)INT32_MAX || (N + 63) / 64 > kMaxGridY) return DA_ERR_UNSUPPORTED;
   for (const da_tensor* t : {&q1, &q2, &k, &v, &out}) {
     const da_status s = check_tensor(*t, 2);
     if (s != DA_OK) return s;
@@ -156,9 +155,6 @@ da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, 
   if (s != DA_OK) return s;
   for (const da_tensor* t : {&q1, &q2, &k, &v})
     if (!rows_fit_32bit(*t, N, 2)) return DA_ERR_UNSUPPORTED;
-  const int ppw = (ppk % 2 == 0) ? 2 : 1;
-  const int64_t gx = (int64_t)B * Hkv * (ppk / ppw);
-  if (gx > (int64_t)INT32_MAX) return DA_ERR_UNSUPPORTED;
 
   da::PrefillParams p{};
   p.q1 = q1.ptr; p.q2 = q2.ptr; p.k1 = k.ptr; p.k2 = k.ptr; p.v = v.ptr; p.out = out.ptr;
@@ -172,7 +168,7 @@ da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, 
   p.eps = 0.f;
   p.out_scale = 1.f;
   p.lam = lambda_args(lam);
-  return hip_status(da::launch_v2_bf16(p, ppw, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(da::launch_v2_bf16(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t diffattn_decode_workspace_bytes(int32_t B, int32_t P, int32_t Hkv, int32_t L, int32_t D,
@@ -218,6 +214,55 @@ da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tenso
   p.ws_ml = p.ws_acc + n_rows * D;
   p.lam = lambda_args(lam);
   return hip_status(da::launch_decode_v2(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t diffattn_decode_v1_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d,
+                                          int32_t num_splits) {
+  if (B <= 0 || H <= 0 || L <= 0 || d != 64) return 0;
+  const int chunk = decode_chunk(B, H, L, num_splits);
+  const int64_t splits = (L + chunk - 1) / chunk;
+  return (size_t)((int64_t)B * H * 2 * splits * (2 * d + 2) * (int64_t)sizeof(float));
+}
+
+da_status diffattn_decode_v1(da_tensor q1, da_tensor q2, da_tensor k1cache, da_tensor k2cache,
+                             da_tensor vcache, da_tensor out, int32_t B, int32_t H, int32_t L,
+                             int32_t d, da_dtype dtype, const da_lambda* lam, float eps,
+                             uint32_t flags, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || L < 0) return DA_ERR_SHAPE;
+  if (B == 0 || H == 0) return DA_OK;
+  if (L == 0) return DA_ERR_SHAPE;  // the new token's own row is always present
+  if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
+  if (d != 64) return d <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return DA_ERR_SHAPE;
+  if ((flags & ~DA_V1_NO_NORM) != 0u) return DA_ERR_UNSUPPORTED;
+  if (B > kMaxGridY || H > kMaxGridY) return DA_ERR_UNSUPPORTED;
+  for (const da_tensor* t : {&q1, &q2, &k1cache, &k2cache, &vcache, &out}) {
+    const da_status s = check_tensor(*t, 2);
+    if (s != DA_OK) return s;
+  }
+  da_status s = check_lambda(lam, 256);
+  if (s != DA_OK) return s;
+  const size_t need = diffattn_decode_v1_workspace_bytes(B, H, L, d, num_splits);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return DA_ERR_WORKSPACE;
+
+  da::DecodeV1Params p{};
+  p.q1 = q1.ptr; p.q2 = q2.ptr; p.k1 = k1cache.ptr; p.k2 = k2cache.ptr; p.v = vcache.ptr;
+  p.out = out.ptr;
+  p.sq1 = strides(q1); p.sq2 = strides(q2); p.sk1 = strides(k1cache); p.sk2 = strides(k2cache);
+  p.sv = strides(vcache); p.so = strides(out);
+  p.B = B; p.H = H; p.L = L;
+  p.chunk = decode_chunk(B, H, L, num_splits);
+  p.splits = (L + p.chunk - 1) / p.chunk;
+  p.norm = (flags & DA_V1_NO_NORM) ? 0 : 1;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  p.eps = eps;
+  p.out_scale = (float)(1.0 - diffattn_lambda_init(lam->layer));
+  const int64_t n_rows = (int64_t)B * H * 2 * p.splits;
+  p.ws_acc = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_acc + n_rows * 2 * d;
+  p.lam = lambda_args(lam);
+  return hip_status(da::launch_decode_v1(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

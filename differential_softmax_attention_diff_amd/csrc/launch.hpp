@@ -8,7 +8,8 @@ namespace da {
 
 hipError_t launch_v1_f32(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_v1_bf16(const PrefillParams& p, hipStream_t stream);
-hipError_t launch_v2_bf16(const PrefillParams& p, int pairs_per_wg, hipStream_t stream);
+hipError_t launch_v2_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode_v2(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_v1(const DecodeV1Params& p, hipStream_t stream);
 
 }  // namespace da

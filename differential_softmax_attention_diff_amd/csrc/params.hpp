@@ -36,7 +36,6 @@ struct PrefillParams {
   int32_t causal;
   int32_t norm;          // V1: apply RMS norm + (1 - lambda_init) scale
   int32_t n_row_blocks;  // query row blocks per (batch, head group)
-  int32_t groups_per_kv; // V2: workgroups per KV head along the pair axis
   int32_t pairs_per_kv;  // V2: P / Hkv
   float scale_log2;      // log2(e) / sqrt(d)
   float scale;           // 1 / sqrt(d)
@@ -59,6 +58,27 @@ struct DecodeParams {
   float scale_log2;
   float* ws_acc;         // [B, 2P, splits, D]
   float* ws_ml;          // [B, 2P, splits, 2]  (running max in score units, sum)
+  LambdaArgs lam;
+};
+
+// One V1 decode step: split-K partial pass + combine pass (norm and scale in the combine).
+struct DecodeV1Params {
+  const void* q1;
+  const void* q2;
+  const void* k1;
+  const void* k2;
+  const void* v;
+  void* out;
+  Strides sq1, sq2, sk1, sk2, sv, so;
+  int32_t B, H, L;
+  int32_t splits;        // key-axis splits per (batch, head)
+  int32_t chunk;         // keys per split (multiple of the block size)
+  int32_t norm;          // apply RMS norm + (1 - lambda_init) scale
+  float scale_log2;
+  float eps;
+  float out_scale;       // 1 - lambda_init
+  float* ws_acc;         // [B, H, 2, splits, 2d]
+  float* ws_ml;          // [B, H, 2, splits, 2]  (running max in score units, sum)
   LambdaArgs lam;
 };
 

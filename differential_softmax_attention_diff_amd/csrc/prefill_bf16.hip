@@ -8,33 +8,38 @@
 //   V2: branches are the two query heads of a pair over one shared KV head; y = O.
 // Neither map is ever written to memory.
 //
-// Design (one pass over K/V per query block):
-//  * A 256-thread workgroup owns a block of query rows; each of its four wavefronts owns 32 query
-//    rows (V1: 4 x 32 rows of one head; V2: 2 pairs x 2 x 32 rows, or 1 pair x 4 x 32 rows).
-//  * K and V tiles of 64 keys stream global -> LDS with buffer loads that write LDS directly
-//    (no staging registers); the buffer range check returns zeros past the last row.  Tiles are
-//    double buffered: the loads of tile t+1 are in flight during the MFMAs of tile t.  LDS rows
-//    are dense and XOR-swizzled for the 64-bank (256 B per clock) LDS: 16-byte chunks of K by
-//    (row >> 1) & 7 (128-byte rows) or row & 15 (256-byte rows), 32-byte chunks of V by
-//    2 (row & 3), so the MFMA operand reads are conflict-free (measured with
-//    SQ_LDS_BANK_CONFLICT).  Per-lane read offsets are computed once, outside the key loop.
+// Design (one pass over K/V per block of 64 query rows):
+//  * A 256-thread workgroup owns 64 query rows of one head (V1) or pair (V2).  Its four
+//    wavefronts are (branch, row half): each runs ONE softmax branch over 32 rows, so it holds
+//    64 fp32 accumulators (32 rows x 128 channels) and only its own branch's Q operand.  That
+//    keeps V1 at 128 VGPRs (4 waves per SIMD) and V2 at under 168 (3 per SIMD); the waves of
+//    different workgroups on a SIMD overlap one another's softmax and MFMA work.
+//  * Tiles of 32 keys stream global -> LDS through buffer loads that write LDS directly (issued
+//    from inline asm, see dma16), double buffered: the loads of tile t+1 are in flight during
+//    the MFMAs of tile t; one barrier per tile.  The buffer range check returns zeros past the
+//    last row.  LDS rows are XOR-swizzled for the 64-bank LDS (16-byte chunks of K by
+//    (row >> 1) & 7 for 128-byte rows or row & 15 for 256-byte rows, 32-byte chunks of V by
+//    2 (row & 3)): the MFMA operand reads are conflict-free (SQ_LDS_BANK_CONFLICT = 0).
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16.  Its accumulator
-//    gives each lane one query column and, per 32-key block, keys {8j + 4h + r}; split into two
-//    16-key halves these are exactly the B operand P^T of O^T = V^T P^T.  The matching V^T
-//    operand comes straight from the row-major V tile with ds_read_b64_tr_b16 (a transposing LDS
-//    read: per 16-lane group, each lane receives one column of a 4-key x 16-channel block).
-//  * Each branch keeps its own online-softmax state per query row.  The running max moves only
-//    when a row's new max exceeds it by more than 2^8 in exp2 units (the accumulators are then
-//    rescaled); otherwise the stale max is kept, which changes no result because numerator and
-//    row sum share it.  exp is exp2 with log2(e)/sqrt(d) folded into one FMA; the row sums add
-//    the rounded weights the MFMA consumes (v_dot2 of packed pairs against 1).
-//  * Epilogue: O = acc_1 / l_1 - lambda acc_2 / l_2, V1 RMS norm + scale, bf16 RNE store.
-//  * Causal: tiles past a wavefront's last row are skipped; only tiles crossing the diagonal or
-//    the ragged end are masked element by element.  Row blocks are issued heaviest first and all
-//    row blocks of one head land on one XCD when the head count is a multiple of 8.
+//    gives each lane one query column and keys {8j + 4h + r}; split into two 16-key halves these
+//    are exactly the B operand P^T of O^T = V^T P^T.  The V^T operand comes straight from the
+//    row-major V tile through ds_read_b64_tr_b16 (a transposing LDS read: per 16-lane group, each
+//    lane receives one column of a 4-key x 16-channel block).
+//  * Online softmax without a per-tile max: weights exp2((s - m) log2(e)/sqrt(d)) are formed
+//    against a per-row reference max m that moves only when a lane's weight sum for the tile
+//    exceeds 2^12 (the first tile, where m is still -1e30, or a score jump); then the tile's
+//    exact max is taken, the accumulators rescaled and the weights formed again.  The row sums
+//    add the rounded weights the MFMA consumes (v_dot2 of packed pairs against 1).
+//  * Epilogue: the branch-2 wave of a row half writes lambda acc_2 / l_2 to LDS; the branch-1
+//    wave forms acc_1 / l_1 minus it, applies the V1 RMS norm and scale, and stores bf16 (RNE).
+//  * Causal: a wave computes tiles up to its last visible key and then only helps load; only
+//    tiles crossing the diagonal or the ragged end are masked element by element.  Row blocks
+//    are issued heaviest first; all row blocks of a head (V1) or all pairs of a KV head (V2)
+//    land on one XCD.
 //  * F16PV (V2): P.V runs on the fp16 MFMA (P and V rounded to fp16, 11 significant bits instead
-//    of bf16's 8).  V is then staged through registers and converted; a V tile holding any
-//    |v| > 65504 stays bf16 and is multiplied on the bf16 MFMA, decided by a workgroup vote.
+//    of bf16's 8).  Each wave stages one 16-key x 64-channel region of the next V tile through
+//    registers and stores it as fp16, or as bf16 when the region holds a value beyond the fp16
+//    range; a per-region flag in LDS sends the wave to a bf16 P.V loop from that tile on.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -43,7 +48,6 @@
 namespace da {
 namespace {
 
-constexpr int kBN = 64;     // keys per tile
 constexpr int kDV = 128;    // value width
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for the running max
@@ -69,10 +73,8 @@ __device__ __forceinline__ int v_off(int row, int col) {
   return row * kDV + ((((col >> 4) ^ (2 * (row & 3)))) << 4) + (col & 15);
 }
 
-// max / sum of x over the lane pair (l, l ^ 32).  (A v_permlane32_swap formulation was tried:
-// the compiler treated both of its results as one value, so the exchange goes through
-// ds_bpermute.)
-__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// sum of x over the lane pair (l, l ^ 32).  (A v_permlane32_swap formulation was tried: the
+// compiler treated both of its results as one value, so lane exchanges go through ds_bpermute.)
 __device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
 
 // Round 8 consecutive weights of s to a packed MFMA operand and add the rounded values to l
@@ -137,7 +139,6 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
-// ------------------------------------------------------------------------------------------------
 constexpr int kSBN = 32;  // keys per tile
 
 template <int DQK, bool V2>
@@ -185,13 +186,17 @@ void prefill_kernel(const PrefillParams p) {
   const int wrow = row0 + 32 * rh;
   const int N = p.N;
 
+  // Blocks are dealt to the 8 XCDs round-robin by linear index and blockIdx.x runs fastest, so
+  // every row block of one head (V1, when 8 divides B*H), or of all pairs over one KV head (V2,
+  // when 8 divides B*Hkv), lands on the same XCD: a head's K/V is shared through one L2.  Row
+  // blocks go heaviest first over all heads, which keeps the causal tail short (a head-major
+  // order measured slower despite 6x less HBM fetch).
   int b, kvh, qh;
   if (!V2) {
     b = blockIdx.x / p.heads;
     qh = blockIdx.x % p.heads;
     kvh = qh;
   } else {
-    // consecutive blocks walk KV heads first, so all pairs of one KV head share an XCD
     const int bk = p.B * p.Hkv;
     const int i = blockIdx.x / bk;
     const int rem = blockIdx.x % bk;
@@ -541,10 +546,9 @@ hipError_t launch_v1_bf16(const PrefillParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_v2_bf16(const PrefillParams& p, int /*pairs_per_wg*/, hipStream_t stream) {
+hipError_t launch_v2_bf16(const PrefillParams& p, hipStream_t stream) {
   PrefillParams q = p;
   q.pairs_per_kv = p.heads / p.Hkv;
-  q.groups_per_kv = q.pairs_per_kv;
   q.n_row_blocks = (p.N + 63) / 64;
   const dim3 grid(p.B * p.heads, q.n_row_blocks);
   hipLaunchKernelGGL((prefill_kernel<128, true, true>), grid, dim3(kThreads), 0, stream, q);

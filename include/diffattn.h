@@ -106,7 +106,7 @@ da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2
  *   out[b,p,i,:] = softmax(q1 k^T / sqrt(D)) v - lambda_p softmax(q2 k^T / sqrt(D)) v
  *   (no normalisation, no scale).
  *
- * Supported: D == 128, dtype DA_BF16, P % Hkv == 0, P / Hkv <= 8.
+ * Supported: D == 128, dtype DA_BF16, P % Hkv == 0.
  */
 da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor out,
                           int32_t B, int32_t P, int32_t Hkv, int32_t N, int32_t D,
@@ -137,6 +137,36 @@ da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tenso
                           da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t L, int32_t D,
                           da_dtype dtype, const da_lambda* lam, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace diffattn_decode_v1 needs for these sizes and split count
+ * (num_splits <= 0 selects the library's default).  Returns 0 for unsupported sizes.
+ */
+size_t diffattn_decode_v1_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d,
+                                          int32_t num_splits);
+
+/*
+ * diffattn_decode_v1 -- one V1 decode step (Ultralytics glossary "Differential Transformer",
+ * section "Cómo funciona la atención diferencial"; ai-engineering.academy "Atención Diferencial
+ * (V2)", section "V1 vs V2: la diferencia", which notes that V1 decode needs the value cache for
+ * both softmax branches).  Each sequence has one new query token (halves q1, q2) whose own K1,
+ * K2, V already sit in cache row L-1; it attends to all L rows.  K1, K2 and V are each read once
+ * per step; one pass over V feeds both branches.
+ *
+ *   q1, q2 : [B, H, d]   (3-D: sb, sh used, sn ignored)     out : [B, H, 2d]
+ *   k1cache, k2cache : [B, H, L, d]    vcache : [B, H, L, 2d]     lambda vectors: [H, dl]
+ *   out[b,h,:] = last row of diffattn_fwd_v1 with N = L (same eps, same flags:
+ *   DA_V1_NO_NORM returns the core (A1 - lambda A2) V row).
+ *   workspace: device buffer of at least diffattn_decode_v1_workspace_bytes(...) bytes, 16-byte
+ *   aligned; its contents on entry do not matter and are clobbered.
+ *
+ * Supported: d == 64, dtype DA_BF16.
+ */
+da_status diffattn_decode_v1(da_tensor q1, da_tensor q2, da_tensor k1cache, da_tensor k2cache,
+                             da_tensor vcache, da_tensor out, int32_t B, int32_t H, int32_t L,
+                             int32_t d, da_dtype dtype, const da_lambda* lam, float eps,
+                             uint32_t flags, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* lambda_init(l) = 0.8 - 0.6 exp(-0.3 (l - 1)) in double precision; NaN for l < 1. */
 double diffattn_lambda_init(int32_t layer);

@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_header_symbols_exported(da):
     names = _declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 9, names
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -105,7 +105,7 @@ def test_v2_and_decode_host_validation(da):
     assert lib.diffattn_fwd_v2(*t5, 1, 4, 2, 8, 128, 0, ctypes.byref(lam), 1, None) == 3  # fp32
     assert lib.diffattn_fwd_v2(*t5, 1, 4, 0, 8, 128, 1, ctypes.byref(lam), 1, None) == 2
     assert lib.diffattn_fwd_v2(*t5, 0, 4, 2, 8, 128, 1, ctypes.byref(lam), 1, None) == 0
-    assert lib.diffattn_fwd_v2(*t5, 1, 32, 2, 8, 128, 1, ctypes.byref(lam), 1, None) == 3  # 16 pairs/KV
+    assert lib.diffattn_fwd_v2(*t5, 1, 1 << 16, 2, 1 << 22, 128, 1, ctypes.byref(lam), 1, None) == 3  # grid
     need = da.diffattn_decode_workspace_bytes(2, 4, 2, 1000, 128)
     assert need > 0
     assert da.diffattn_decode_workspace_bytes(2, 3, 2, 1000, 128) == 0
@@ -127,6 +127,40 @@ def test_decode_workspace_size_formula(da):
     assert da.diffattn_decode_workspace_bytes(1, 1, 1, 1000, 128, 50) == 2 * 4 * 130 * 4
     b = da.diffattn_decode_workspace_bytes(64, 16, 8, 32768, 128, 0)
     assert b == 64 * 32 * 8 * 130 * 4
+
+
+def test_decode_v1_host_validation(da):
+    lib = da.load_library()
+    t6 = [_t() for _ in range(6)]
+    lam = _lam(dl=64)
+    need = da.diffattn_decode_v1_workspace_bytes(2, 4, 1000, 64)
+    assert need > 0
+    assert da.diffattn_decode_v1_workspace_bytes(2, 4, 1000, 128) == 0   # d != 64
+    dec = lambda ws, nbytes, B=2, H=4, L=1000, d=64, dt=1, eps=1e-5, flags=0, lam=lam: \
+        lib.diffattn_decode_v1(*t6, B, H, L, d, dt, ctypes.byref(lam), eps, flags, 0, ws, nbytes, None)
+    assert dec(None, need) == 4                              # no workspace
+    assert dec(0x30000, need - 1) == 4                       # too small
+    assert dec(0x30008, need) == 4                           # misaligned workspace
+    assert dec(0x30000, need, d=128) == 3
+    assert dec(0x30000, need, d=0) == 2
+    assert dec(0x30000, need, dt=0) == 3                     # fp32
+    assert dec(0x30000, need, L=0) == 2
+    assert dec(0x30000, need, B=-1) == 2
+    assert dec(0x30000, need, B=0) == 0
+    assert dec(0x30000, need, eps=float("nan")) == 2
+    assert dec(0x30000, need, flags=2) == 3
+    assert dec(0x30000, need, lam=_lam(layer=0)) == 2
+    bad = [_t() for _ in range(6)]
+    bad[2] = _t(ptr=0x10008)                                 # misaligned K1 cache
+    assert lib.diffattn_decode_v1(*bad, 2, 4, 1000, 64, 1, ctypes.byref(lam), 1e-5, 0, 0, 0x30000,
+                                  need, None) == 1
+
+
+def test_decode_v1_workspace_size_formula(da):
+    # B * H * 2 branches * splits * (2d + 2) floats; at most one split per 256 keys
+    assert da.diffattn_decode_v1_workspace_bytes(1, 1, 100, 64, 0) == 1 * 2 * 1 * 130 * 4
+    assert da.diffattn_decode_v1_workspace_bytes(1, 1, 1000, 64, 3) == 2 * 2 * 130 * 4
+    assert da.diffattn_decode_v1_workspace_bytes(32, 16, 32768, 64, 0) == 32 * 16 * 2 * 8 * 130 * 4
 
 
 def test_binding_refuses_cpu_tensors(da):

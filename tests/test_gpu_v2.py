@@ -43,13 +43,14 @@ def _oracle_v2(t, layer, causal=True, rows=None, pairs=None, batches=None):
 
 
 @pytest.mark.parametrize("B,P,Hkv,N,causal", [
-    (1, 1, 1, 1, True),       # one pair per KV head (single-pair workgroups)
+    (1, 1, 1, 1, True),       # one pair per KV head, one key
     (1, 3, 3, 100, True),
     (2, 2, 1, 64, False),     # two pairs per KV head
-    (1, 4, 2, 129, True),
+    (1, 4, 2, 129, True),     # ragged tail one past a 64-row block
     (2, 8, 2, 200, True),     # four pairs per KV head
     (1, 16, 8, 333, True),    # the workload's head layout at a short length
-    (1, 6, 2, 150, False),    # three pairs per KV head (odd: single-pair workgroups)
+    (1, 6, 2, 150, False),    # three pairs per KV head
+    (1, 16, 1, 97, True),     # sixteen pairs over a single KV head
 ])
 def test_v2_full_compare(da, B, P, Hkv, N, causal):
     log(f"v2 B={B} P={P} Hkv={Hkv} N={N} causal={causal}")

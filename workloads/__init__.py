@@ -14,9 +14,10 @@ round-to-nearest-even; the oracle reads exactly those bf16 values.
 
 Workloads
 ---------
-``CONFIGS`` lists the five workloads: a small fp32 V1 case, the V1 prefill at a 4K context,
-the V2 (GQA, paired query heads) prefill at 8K, the V2 decode step over a 32K-token cache and the
-V1 long-context prefill at 128K tokens with planted "needle" keys.
+``CONFIGS`` lists the workloads: a small fp32 V1 case, the V1 prefill at a 4K context, the V2
+(GQA, paired query heads) prefill at 8K, the V2 decode step over a 32K-token cache, the V1
+long-context prefill at 128K tokens with planted "needle" keys, and the V1-layout decode step
+over a 32K-token cache (its K1 + K2 + V cache is as large as the V2 decode's K + V cache).
 """
 
 from __future__ import annotations
@@ -41,6 +42,8 @@ CONFIGS = {
                           layers=(24,), seed=1004),
     "v1_long_128k": dict(kind="v1", dtype="bf16", B=1, H=16, N=131072, d=64, causal=True,
                          layers=tuple(range(1, 33)), eps=1e-5, needles=6, seed=1005),
+    "v1_decode_32k": dict(kind="decode_v1", dtype="bf16", B=32, H=16, L=32768, d=64,
+                          layers=(12,), eps=1e-5, seed=1006),
 }
 
 _TAGS = {"q1": 1, "q2": 2, "k1": 3, "k2": 4, "v": 5, "q": 6, "k": 7,
@@ -177,6 +180,19 @@ def make_decode(B, P, Hkv, L, D, dtype="bf16", seed=0, layers=(1,)):
     }
 
 
+def make_decode_v1(B, H, L, d, dtype="bf16", seed=0, layers=(1,)):
+    """V1 decode inputs: q1, q2 [B, H, d] (one new token per sequence); k1cache, k2cache
+    [B, H, L, d]; vcache [B, H, L, 2d]."""
+    return {
+        "q1": normal_tensor(seed, "q1", (B, H, 1, d), dtype)[:, :, 0, :].copy(),
+        "q2": normal_tensor(seed, "q2", (B, H, 1, d), dtype)[:, :, 0, :].copy(),
+        "k1cache": normal_tensor(seed, "k1", (B, H, L, d), dtype),
+        "k2cache": normal_tensor(seed, "k2", (B, H, L, d), dtype),
+        "vcache": normal_tensor(seed, "v", (B, H, L, 2 * d), dtype),
+        "lambda": {l: lambda_vectors(seed, H, d, l) for l in layers},
+    }
+
+
 def make(name: str, **overrides):
     """Inputs of a named workload (``CONFIGS``), with optional shape overrides."""
     cfg = dict(CONFIGS[name])
@@ -191,4 +207,7 @@ def make(name: str, **overrides):
     if kind == "decode":
         return cfg, make_decode(cfg["B"], cfg["P"], cfg["Hkv"], cfg["L"], cfg["D"], cfg["dtype"],
                                 cfg["seed"], cfg["layers"])
+    if kind == "decode_v1":
+        return cfg, make_decode_v1(cfg["B"], cfg["H"], cfg["L"], cfg["d"], cfg["dtype"], cfg["seed"],
+                                   cfg["layers"])
     raise KeyError(kind)
