@@ -140,8 +140,11 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 }
 
 constexpr int kSBN = 32;  // keys per tile
+// Tile buffers in LDS.  Three (loads two tiles ahead) measured 7 % slower for V1: 48 KB per
+// workgroup allows 3 workgroups per CU instead of 4, and load latency was not the limit.
+constexpr int kStagesV1 = 2;
 
-template <int DQK, bool V2>
+template <int DQK, bool V2, int NS>
 struct SCfg {
   static constexpr int NK = V2 ? 1 : 2;                 // K tensors per tile (V2: one shared K)
   static constexpr int K_ELEMS = kSBN * DQK;            // one K tensor tile
@@ -150,7 +153,7 @@ struct SCfg {
   static constexpr int K_LOADS = K_ELEMS * 2 / 1024;    // 1 KB wavefront DMA loads per K tile
   static constexpr int V_LOADS = VBUF * 2 / 1024;
   static constexpr int TQ = DQK / 16;                   // MFMA k-steps over the head width
-  static constexpr int SMEM = 2 * KBUF + 2 * VBUF;      // [K0 | K1 | V0 | V1]
+  static constexpr int SMEM = NS * (KBUF + VBUF);       // [K0 .. K(NS-1) | V0 .. V(NS-1)]
 };
 
 // 8 packed fp16 values -> 8 packed bf16 values (RNE)
@@ -162,17 +165,16 @@ __device__ __forceinline__ u32x4 f16x8_to_bf16x8(u32x4 x) {
   return __builtin_bit_cast(u32x4, r);
 }
 
-template <int DQK, bool V2, bool F16PV>
+template <int DQK, bool V2, bool F16PV, int NS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(V2 ? 3 : 4)))
 void prefill_kernel(const PrefillParams p) {
-  using C = SCfg<DQK, V2>;
+  using C = SCfg<DQK, V2, NS>;
   constexpr int BM = 64;
   __shared__ __attribute__((aligned(1024))) bf16 smem[C::SMEM];
-  __shared__ int vflag[2][4];
+  __shared__ int vflag[NS][4];
   static_assert(C::SMEM * 2 >= 2 * 64 * 64 * 4, "epilogue exchange must fit the tile buffers");
-  static_assert(C::KBUF == C::VBUF && ((C::KBUF * 2) & (C::KBUF * 2 - 1)) == 0,
-                "buffers flip by XOR of one power of two");
-  constexpr uint32_t kFlip = C::KBUF * 2;  // bytes between the two buffers of K (and of V)
+  static_assert(!F16PV || NS == 2, "F16PV converts the next tile's V in the same iteration");
+  constexpr uint32_t kKB = C::KBUF * 2, kVB = C::VBUF * 2;  // bytes per K / V buffer
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -283,7 +285,7 @@ void prefill_kernel(const PrefillParams p) {
     const int rows_left = N - kt;
     const __amdgpu_buffer_rsrc_t rvt = make_rsrc(v_base + (size_t)kt * v_row, (uint32_t)rows_left * v_row);
     if constexpr (!F16PV) {
-      bf16* vb = smem + 2 * C::KBUF + buf * C::VBUF;
+      bf16* vb = smem + NS * C::KBUF + buf * C::VBUF;
 #pragma unroll
       for (int i = 0; i < VPW; ++i) dma16(rvt, vb + 512 * (w + 4 * i), v_lane[i]);
     } else {
@@ -294,7 +296,7 @@ void prefill_kernel(const PrefillParams p) {
   // F16PV: convert the staged region (unless it holds a value fp16 cannot represent), store it,
   // and publish the region's format
   auto finish_v = [&](int buf) {
-    bf16* vb = smem + 2 * C::KBUF + buf * C::VBUF;
+    bf16* vb = smem + NS * C::KBUF + buf * C::VBUF;
     float mx = 0.f;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -314,8 +316,8 @@ void prefill_kernel(const PrefillParams p) {
     if (lane == 0) vflag[buf][w] = big ? 1 : 0;
   };
   auto issue_tile = [&](int i) {
-    issue_k(i * kSBN, i & 1);
-    issue_v(i * kSBN, i & 1);
+    issue_k(i * kSBN, i % NS);
+    issue_v(i * kSBN, i % NS);
   };
 
   f32x16 acc[4];
@@ -338,7 +340,7 @@ void prefill_kernel(const PrefillParams p) {
   {
     const int j = lane & 15, dh = (lane >> 4) & 1;
     const int row = 4 * hh + (j >> 2);
-    v_ad = 2u * (2 * C::KBUF + v_off(row, dh * 16 + 4 * (j & 3)));
+    v_ad = 2u * (NS * C::KBUF + v_off(row, dh * 16 + 4 * (j & 3)));
   }
   const char* sb = reinterpret_cast<const char*>(smem);
   // max over the lane pair (l, l ^ 32) through ds_bpermute with a loop-invariant address
@@ -348,17 +350,17 @@ void prefill_kernel(const PrefillParams p) {
   };
 
   // K operand t of the next score tile; V^T operand db, lower or upper read, 16-key group u
-  auto k_operand = [&](int t) { return *reinterpret_cast<const bf16x8*>(sb + (k_ad ^ (32u * t))); };
-  auto v_read = [&](int db, int u, int upper) {
-    return lds_read_tr(reinterpret_cast<const bf16*>(sb + (v_ad ^ (64u * db))) + (16 * u + 8 * upper) * kDV);
+  auto k_operand = [&](uint32_t kb, int t) { return *reinterpret_cast<const bf16x8*>(sb + (kb ^ (32u * t))); };
+  auto v_read = [&](uint32_t vb, int db, int u, int upper) {
+    return lds_read_tr(reinterpret_cast<const bf16*>(sb + (vb ^ (64u * db))) + (16 * u + 8 * upper) * kDV);
   };
 
-  auto scores = [&]() {
+  auto scores = [&](uint32_t kb) {
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int t = 0; t < C::TQ; ++t) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(t), qf[t], s, 0, 0, 0);
+    for (int t = 0; t < C::TQ; ++t) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(kb, t), qf[t], s, 0, 0, 0);
     return s;
   };
   // causal diagonal and ragged end only
@@ -375,12 +377,12 @@ void prefill_kernel(const PrefillParams p) {
   // weights exp2((s - m) log2(e) / sqrt(d)) for the reference max m, rounded to the two packed
   // P operands (16 keys each); tl gets the lane's sum of the rounded weights
   using POp = std::conditional_t<F16PV, f16x8, bf16x8>;
-  auto weights = [&](const f32x16& s, POp& p0, POp& p1, float& tl, auto half_tag) {
+  // (s is overwritten by the weights; the rare slow path forms the scores again from LDS)
+  auto weights = [&](f32x16& e, POp& p0, POp& p1, float& tl, auto half_tag) {
     constexpr bool kHalf = decltype(half_tag)::value;
     const float nm = -mrun * sl2;
-    f32x16 e;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nm));
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(e[r], sl2, nm));
     tl = 0.f;
     if constexpr (kHalf) {
       p0 = __builtin_bit_cast(POp, cvt8h_sum(e, 0, tl));
@@ -402,14 +404,22 @@ void prefill_kernel(const PrefillParams p) {
     constexpr bool kSlow = decltype(slow_tag)::value;
     constexpr bool kHalf = F16PV && !kSlow;
     const int kt = i * kSBN;
+    const int buf = i % NS;
+    const uint32_t kb = k_ad + buf * kKB;  // this tile's buffers (the swizzle XORs touch bits < 13)
+    const uint32_t vb = v_ad + buf * kVB;
     __builtin_amdgcn_s_setprio(1);
-    f32x16 s = scores();
+    f32x16 s = scores(kb);
     __builtin_amdgcn_s_setprio(0);
     mask(s, kt);
     POp p0, p1;
     float tl;
     weights(s, p0, p1, tl, std::integral_constant<bool, kHalf>{});
     if (__any(!(tl <= kCapSum))) {
+      // the K tile of this step is still in its buffer: form the scores again
+      __builtin_amdgcn_s_setprio(1);
+      s = scores(kb);
+      __builtin_amdgcn_s_setprio(0);
+      mask(s, kt);
       float mx = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -425,15 +435,15 @@ void prefill_kernel(const PrefillParams p) {
     lrun += tl;
 
     // O^T += V^T P^T, 16 keys per MFMA
-    const int vbuf = i & 1;
+    const int vbuf = buf;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const POp pp = u == 0 ? p0 : p1;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const u32x2 lo = v_read(db, u, 0);
-        const u32x2 hi = v_read(db, u, 1);
+        const u32x2 lo = v_read(vb, db, u, 0);
+        const u32x2 hi = v_read(vb, db, u, 1);
         u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
         if constexpr (kHalf) {
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a4), pp, acc[db], 0, 0, 0);
@@ -449,8 +459,6 @@ void prefill_kernel(const PrefillParams p) {
       }
     }
     __builtin_amdgcn_s_setprio(0);
-    k_ad ^= kFlip;
-    v_ad ^= kFlip;
   };
 
   // ---- main loop: loads of tile t+1 are in flight during the MFMAs of tile t.  A wave computes
@@ -459,22 +467,46 @@ void prefill_kernel(const PrefillParams p) {
   // with a bf16 region on, a wave stays on the bf16 path, in a loop of its own so that the
   // accumulators never merge from two paths inside one loop.
   auto tile_big = [&](int i) {
-    const int vb = i & 1;
+    const int vb = i % NS;
     return F16PV && (vflag[vb][0] | vflag[vb][1] | vflag[vb][2] | vflag[vb][3]) != 0;
   };
+  // Iteration i loads tile i + NS - 1 into the buffer tile i - 1 used, computes tile i, and waits
+  // until tile i + 1 has landed: with NS > 2 the loads of the tiles after it stay in flight
+  // (vmcnt counts this wave's outstanding buffer loads, which complete in order).
+  constexpr int kLoadsPerTile = C::NK * KPW + VPW;  // DMA instructions per wave per tile
+  auto wait_next = [&](int i) {
+    if constexpr (NS == 2 || F16PV) {
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      static_assert(NS == 3, "vmcnt for one younger tile in flight");
+      if (i + 2 < ntiles) __builtin_amdgcn_s_waitcnt(kLoadsPerTile | (7 << 4) | (15 << 8));
+      else __builtin_amdgcn_s_waitcnt(0);
+    }
+  };
   auto step = [&](int i, auto slow_tag) {
-    const bool more = i + 1 < ntiles;
-    if (more) issue_tile(i + 1);
+    const int ahead = i + NS - 1;
+    const bool more = ahead < ntiles;
+    if (more) issue_tile(ahead);
     compute_tile(i, slow_tag);
     if constexpr (F16PV) {
-      if (more) finish_v((i + 1) & 1);
+      if (more) finish_v(ahead % NS);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    wait_next(i);
     __syncthreads();
   };
-  issue_tile(0);
-  if constexpr (F16PV) finish_v(0);
-  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) {
+    if (i < ntiles) {
+      issue_tile(i);
+      if constexpr (F16PV) finish_v(i);
+    }
+  }
+  if constexpr (NS == 2 || F16PV) {
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
+    if (ntiles > 1) __builtin_amdgcn_s_waitcnt(kLoadsPerTile | (7 << 4) | (15 << 8));
+    else __builtin_amdgcn_s_waitcnt(0);
+  }
   __syncthreads();
   int it = 0;
   for (; it < nt_wave; ++it) {
@@ -485,11 +517,12 @@ void prefill_kernel(const PrefillParams p) {
     for (; it < nt_wave; ++it) step(it, std::true_type{});
   }
   for (; it < ntiles; ++it) {
-    if (it + 1 < ntiles) {
-      issue_tile(it + 1);
-      if constexpr (F16PV) finish_v((it + 1) & 1);
+    const int ahead = it + NS - 1;
+    if (ahead < ntiles) {
+      issue_tile(ahead);
+      if constexpr (F16PV) finish_v(ahead % NS);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    wait_next(it);
     __syncthreads();
   }
 
@@ -542,7 +575,7 @@ hipError_t launch_v1_bf16(const PrefillParams& p, hipStream_t stream) {
   PrefillParams q = p;
   q.n_row_blocks = (p.N + 63) / 64;
   const dim3 grid(p.B * p.heads, q.n_row_blocks);
-  hipLaunchKernelGGL((prefill_kernel<64, false, false>), grid, dim3(kThreads), 0, stream, q);
+  hipLaunchKernelGGL((prefill_kernel<64, false, false, kStagesV1>), grid, dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 
@@ -551,7 +584,7 @@ hipError_t launch_v2_bf16(const PrefillParams& p, hipStream_t stream) {
   q.pairs_per_kv = p.heads / p.Hkv;
   q.n_row_blocks = (p.N + 63) / 64;
   const dim3 grid(p.B * p.heads, q.n_row_blocks);
-  hipLaunchKernelGGL((prefill_kernel<128, true, true>), grid, dim3(kThreads), 0, stream, q);
+  hipLaunchKernelGGL((prefill_kernel<128, true, true, 2>), grid, dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 
