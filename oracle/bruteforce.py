@@ -25,32 +25,35 @@ def dot(a, b):
     return sum(x * y for x, y in zip(a, b))
 
 
-def _weights(q, keys, i, causal, scale):
-    n_vis = i + 1 if causal else len(keys)
-    w = softmax([dot(q, keys[j]) / scale for j in range(n_vis)])
-    return w + [0.0] * (len(keys) - n_vis)
+def _weights(q, keys, i, causal, scale, window=0):
+    """Softmax weights of query row i over the keys it may see, zeros elsewhere.  With a window
+    W > 0 (causal only) row i sees keys i - W + 1 .. i."""
+    last = i if causal else len(keys) - 1
+    first = max(0, i - window + 1) if window else 0
+    w = softmax([dot(q, keys[j]) / scale for j in range(first, last + 1)])
+    return [0.0] * first + w + [0.0] * (len(keys) - 1 - last)
 
 
-def diff_attention(Q1, K1, Q2, K2, V, lam, causal=False):
+def diff_attention(Q1, K1, Q2, K2, V, lam, causal=False, window=0):
     """(A1 - lam * A2) V for one head; all arguments are lists of lists of floats."""
     scale = math.sqrt(len(Q1[0]))
     d_v = len(V[0])
     out = []
     for i in range(len(Q1)):
-        a1 = _weights(Q1[i], K1, i, causal, scale)
-        a2 = _weights(Q2[i], K2, i, causal, scale)
+        a1 = _weights(Q1[i], K1, i, causal, scale, window)
+        a2 = _weights(Q2[i], K2, i, causal, scale, window)
         w = [x - lam * y for x, y in zip(a1, a2)]
         out.append([sum(wj * V[j][c] for j, wj in enumerate(w)) for c in range(d_v)])
     return out
 
 
-def attention(Q, K, V, causal=False):
+def attention(Q, K, V, causal=False, window=0):
     """Plain softmax attention softmax(Q K^T / sqrt(d)) V for one head."""
     scale = math.sqrt(len(Q[0]))
     d_v = len(V[0])
     out = []
     for i in range(len(Q)):
-        w = _weights(Q[i], K, i, causal, scale)
+        w = _weights(Q[i], K, i, causal, scale, window)
         out.append([sum(wj * V[j][c] for j, wj in enumerate(w)) for c in range(d_v)])
     return out
 

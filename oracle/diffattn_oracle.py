@@ -20,6 +20,9 @@ Sources (web pages; cited by title and section):
 Readings taken where the pages are silent or ambiguous (each is listed in the design doc too):
   * d inside sqrt(d) is the per-branch query/key width ([G] example divides by the half width).
   * causal: key j is visible to query i iff j <= i (square, N_q == N_k); masked weights are 0.
+  * sliding window W (the window layers of the hybrid DIFF / sliding-window stacks that [L]
+    "Úselo" mentions): causal, and key j is visible to query i only if i - W < j, so each row
+    sees its last W positions including itself.  W = 0 means no window.
   * one lambda per head (V1) or per head pair (V2), from rows of four [H, d] vectors.
   * lambda_init uses the 1-based layer index; the V1 norm is RMS (no mean subtraction, no gain),
     eps inside the square root, applied before the (1 - lambda_init) scale; V2 has neither.
@@ -94,14 +97,19 @@ def softmax_rows(scores: np.ndarray, visible: np.ndarray | None = None) -> np.nd
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
-def _visible(rows: np.ndarray, n_keys: int, causal: bool) -> np.ndarray | None:
+def _visible(rows: np.ndarray, n_keys: int, causal: bool, window: int = 0) -> np.ndarray | None:
+    if window and not causal:
+        raise ValueError("a sliding window is defined for causal attention only")
     if not causal:
         return None
     keys = np.arange(n_keys)
-    return keys[None, :] <= rows[:, None]
+    vis = keys[None, :] <= rows[:, None]
+    if window:
+        vis &= keys[None, :] > rows[:, None] - window
+    return vis
 
 
-def diff_maps(q1, k1, q2, k2, lam: float, causal: bool = False):
+def diff_maps(q1, k1, q2, k2, lam: float, causal: bool = False, window: int = 0):
     """Both softmax maps of one head and their lambda-weighted difference.
 
     A1 = softmax(Q1 K1^T / sqrt(d)), A2 = softmax(Q2 K2^T / sqrt(d)), W = A1 - lam * A2,
@@ -112,7 +120,7 @@ def diff_maps(q1, k1, q2, k2, lam: float, causal: bool = False):
     q1, k1, q2, k2 = (np.asarray(a, dtype=np.float64) for a in (q1, k1, q2, k2))
     d = q1.shape[-1]
     rows = np.arange(q1.shape[0])
-    vis = _visible(rows, k1.shape[0], causal)
+    vis = _visible(rows, k1.shape[0], causal, window)
     a1 = softmax_rows(q1 @ k1.T / math.sqrt(d), vis)
     a2 = softmax_rows(q2 @ k2.T / math.sqrt(d), vis)
     return a1, a2, a1 - lam * a2
@@ -133,7 +141,7 @@ def _rows_arg(rows, n: int) -> np.ndarray:
     return rows
 
 
-def diff_core_rows(q1, k1, q2, k2, v, lam: float, causal: bool, rows=None) -> np.ndarray:
+def diff_core_rows(q1, k1, q2, k2, v, lam: float, causal: bool, rows=None, window: int = 0) -> np.ndarray:
     """Un-normalised differential attention (A1 - lam * A2) V for chosen query rows of one head.
 
     [L] "La idea diferencial" (DiffAttn = (A_1 - lambda A_2) V) and "Implementación" step 3;
@@ -150,7 +158,7 @@ def diff_core_rows(q1, k1, q2, k2, v, lam: float, causal: bool, rows=None) -> np
     pos = 0
     for blk in _row_blocks(rows, n_k):
         kmax = int(blk.max()) + 1 if causal else n_k
-        vis = _visible(blk, kmax, causal)
+        vis = _visible(blk, kmax, causal, window)
         a1 = softmax_rows(q1[blk] @ k1[:kmax].T / math.sqrt(d), vis)
         a2 = softmax_rows(q2[blk] @ k2[:kmax].T / math.sqrt(d), vis)
         out[pos : pos + blk.size] = (a1 - lam * a2) @ v[:kmax]
@@ -158,7 +166,7 @@ def diff_core_rows(q1, k1, q2, k2, v, lam: float, causal: bool, rows=None) -> np
     return out
 
 
-def branch_rows(q, k, v, causal: bool, rows=None) -> np.ndarray:
+def branch_rows(q, k, v, causal: bool, rows=None, window: int = 0) -> np.ndarray:
     """One ordinary softmax-attention branch softmax(q k^T / sqrt(d)) v for chosen query rows.
 
     Used by the V2 layout, where every query head of a pair runs plain softmax attention
@@ -172,7 +180,7 @@ def branch_rows(q, k, v, causal: bool, rows=None) -> np.ndarray:
     pos = 0
     for blk in _row_blocks(rows, n_k):
         kmax = int(blk.max()) + 1 if causal else n_k
-        vis = _visible(blk, kmax, causal)
+        vis = _visible(blk, kmax, causal, window)
         a = softmax_rows(q[blk] @ k[:kmax].T / math.sqrt(d), vis)
         out[pos : pos + blk.size] = a @ v[:kmax]
         pos += blk.size
@@ -190,14 +198,16 @@ def rms_norm_rows(o: np.ndarray, eps: float) -> np.ndarray:
 
 
 def diff_attn_v1(q1, q2, k1, k2, v, lam, lam_init: float, causal: bool = True,
-                 eps: float = 1e-5, norm: bool = True, rows=None, heads=None, batches=None):
+                 eps: float = 1e-5, norm: bool = True, rows=None, heads=None, batches=None,
+                 window: int = 0):
     """V1 layout: per head, (A1 - lam_h A2) V, then RMS norm and the (1 - lam_init) scale.
 
     Shapes: q1, q2, k1, k2 [B, H, N, d]; v [B, H, N, 2d]; lam [H] (one lambda per head).
     [G] "Cómo funciona la atención diferencial" (half the heads, V twice as wide, per-head
     normalisation then scaling by one minus the initial lambda); [L] "V1 vs V2: la diferencia".
     ``norm=False`` returns the core (A1 - lam A2) V without normalisation or scale.
-    ``rows``/``heads``/``batches`` restrict the evaluation (default: all).
+    ``rows``/``heads``/``batches`` restrict the evaluation (default: all).  ``window`` > 0
+    restricts each row to its last ``window`` positions (causal sliding window).
     Returns float64 [len(batches), len(heads), len(rows), 2d].
     """
     b_list = range(q1.shape[0]) if batches is None else list(batches)
@@ -208,14 +218,15 @@ def diff_attn_v1(q1, q2, k1, k2, v, lam, lam_init: float, causal: bool = True,
     for bi, b in enumerate(b_list):
         for hi, h in enumerate(h_list):
             o = diff_core_rows(q1[b, h], k1[b, h], q2[b, h], k2[b, h], v[b, h],
-                               float(lam[h]), causal, rows)
+                               float(lam[h]), causal, rows, window)
             if norm:
                 o = rms_norm_rows(o, eps) * (1.0 - lam_init)
             out[bi, hi] = o
     return out
 
 
-def diff_attn_v2(q, k, v, lam, causal: bool = True, rows=None, pairs=None, batches=None):
+def diff_attn_v2(q, k, v, lam, causal: bool = True, rows=None, pairs=None, batches=None,
+                 window: int = 0):
     """V2 layout: query heads doubled and paired over shared KV heads, pair outputs subtracted.
 
     q [B, 2P, N, D]; k, v [B, Hkv, N, D]; lam [P].  Pair p uses query heads 2p and 2p+1, both
@@ -236,8 +247,8 @@ def diff_attn_v2(q, k, v, lam, causal: bool = True, rows=None, pairs=None, batch
     for bi, b in enumerate(b_list):
         for pi, p in enumerate(p_list):
             g = p * hkv // n_pairs
-            oa = branch_rows(q[b, 2 * p], k[b, g], v[b, g], causal, rows)
-            ob = branch_rows(q[b, 2 * p + 1], k[b, g], v[b, g], causal, rows)
+            oa = branch_rows(q[b, 2 * p], k[b, g], v[b, g], causal, rows, window)
+            ob = branch_rows(q[b, 2 * p + 1], k[b, g], v[b, g], causal, rows, window)
             out[bi, pi] = oa - float(lam[p]) * ob
     return out
 

@@ -374,7 +374,7 @@ def test_row_blocking_does_not_change_values(monkeypatch):
 # ------------------------------------------------------------------------------------------------
 
 def _mutant_core(kind):
-    def core(q1, k1, q2, k2, v, lam, causal, rows=None):
+    def core(q1, k1, q2, k2, v, lam, causal, rows=None, window=0):
         q1, k1, q2, k2, v = (np.asarray(a, dtype=np.float64) for a in (q1, k1, q2, k2, v))
         d = q1.shape[-1]
         n = q1.shape[0]
@@ -436,3 +436,92 @@ def test_mutated_scale_in_v1_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "diff_attn_v1", mutant)
     with pytest.raises(AssertionError):
         test_v1_output_rms_and_scale_uses_lambda_init()
+
+
+# ------------------------------------------------------------------------------------------------
+# sliding window (causal; row i sees its last W positions)
+# ------------------------------------------------------------------------------------------------
+
+def _band(n, window):
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return torch.from_numpy((j <= i) & (j > i - window))
+
+
+def test_window_against_library_sdpa_with_band_mask():
+    """Both branches as library SDPA calls restricted by an explicit band mask."""
+    rng = _rng(31)
+    q1, q2, k1, k2, v = _heads(rng, 1, 3, 40, 64, 128)
+    lam = np.array([0.7, -0.2, 1.1])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    for window in (1, 3, 17, 39, 40, 64):
+        m = _band(40, window)
+        ref = (F.scaled_dot_product_attention(t(q1), t(k1), t(v), attn_mask=m).numpy()
+               - lam[None, :, None, None] * F.scaled_dot_product_attention(t(q2), t(k2), t(v), attn_mask=m).numpy())
+        got = oracle.diff_attn_v1(q1, q2, k1, k2, v, lam, 0.5, True, norm=False, window=window)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_window_of_one_sees_only_itself():
+    """W = 1: both maps are the identity, so the core is (1 - lambda) V row by row."""
+    rng = _rng(32)
+    q1, q2, k1, k2, v = _heads(rng, 1, 2, 25, 64, 128)
+    lam = np.array([0.3, 1.4])
+    got = oracle.diff_attn_v1(q1, q2, k1, k2, v, lam, 0.5, True, norm=False, window=1)
+    np.testing.assert_allclose(got, (1 - lam)[None, :, None, None] * v, rtol=0, atol=1e-13)
+    qv = np.concatenate([q1, q2], axis=1)
+    g2 = oracle.diff_attn_v2(qv[:, [0, 2, 1, 3]], k1[:, :1], v[:, :1], lam, True, window=1)
+    np.testing.assert_allclose(g2, (1 - lam)[None, :, None, None] * v[:, :1], rtol=0, atol=1e-13)
+
+
+def test_window_covering_every_row_is_plain_causal():
+    rng = _rng(33)
+    q1, q2, k1, k2, v = _heads(rng, 1, 2, 30, 16, 32)
+    a = oracle.diff_attn_v1(q1, q2, k1, k2, v, np.array([0.4, 0.6]), 0.5, True)
+    for window in (30, 31, 1000):
+        b = oracle.diff_attn_v1(q1, q2, k1, k2, v, np.array([0.4, 0.6]), 0.5, True, window=window)
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("n", [1, 6, 13])
+def test_window_brute_force_agreement(n):
+    rng = _rng(300 + n)
+    d = 8
+    q1, q2, k1, k2, v = (a[0, 0] for a in _heads(rng, 1, 1, n, d, 2 * d))
+    for window in range(1, n + 2):
+        ref = bfm.diff_attention(q1.tolist(), k1.tolist(), q2.tolist(), k2.tolist(), v.tolist(),
+                                 0.7, True, window)
+        got = oracle.diff_core_rows(q1, k1, q2, k2, v, 0.7, True, window=window)
+        np.testing.assert_allclose(got, np.array(ref), rtol=0, atol=1e-12)
+        refb = bfm.attention(q1.tolist(), k1.tolist(), v.tolist(), True, window)
+        gotb = oracle.branch_rows(q1, k1, v, True, window=window)
+        np.testing.assert_allclose(gotb, np.array(refb), rtol=0, atol=1e-12)
+
+
+def test_window_requires_causal():
+    rng = _rng(34)
+    q1, q2, k1, k2, v = _heads(rng, 1, 1, 8, 8, 16)
+    with pytest.raises(ValueError):
+        oracle.diff_attn_v1(q1, q2, k1, k2, v, np.array([0.5]), 0.5, False, window=4)
+
+
+@pytest.mark.parametrize("kind", ["off_by_one_wide", "off_by_one_narrow"])
+def test_window_mutations_are_caught(kind, monkeypatch):
+    real = orc._visible
+
+    def mutant(rows, n_keys, causal, window=0):
+        if not window:
+            return real(rows, n_keys, causal, window)
+        keys = np.arange(n_keys)
+        vis = keys[None, :] <= rows[:, None]
+        lo = rows[:, None] - window + (-1 if kind == "off_by_one_wide" else 1)
+        return vis & (keys[None, :] > lo)
+
+    monkeypatch.setattr(orc, "_visible", mutant)
+    caught = 0
+    for pin in (test_window_against_library_sdpa_with_band_mask, test_window_of_one_sees_only_itself):
+        try:
+            pin()
+        except (AssertionError, ValueError):  # a wrong value, or a row left with no key
+            caught += 1
+    assert caught > 0, f"window mutation {kind!r} slipped through"
