@@ -177,6 +177,37 @@ def bench_decode(da, torch, steps, warmup):
     }
 
 
+def window_pairs(n, w):
+    """Visible (query, key) pairs of a causal sliding window of w keys over n rows."""
+    w = min(w, n)
+    return w * (w + 1) // 2 + (n - w) * w
+
+
+def bench_swa(da, torch, steps, warmup):
+    cfg, t = wl.make("v1_swa_4k")
+    layer, window = cfg["layers"][0], cfg["window"]
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    args = [to_dev(t[k], torch) for k in ("q1", "q2", "k1", "k2", "v")]
+    lv = [torch.from_numpy(x).to("cuda") for x in t["lambda"][layer]]
+    out = torch.empty((B, H, N, 2 * d), dtype=torch.bfloat16, device="cuda")
+    fn = lambda: da.diffattn_fwd_v1(*args, *lv, layer=layer, out=out, window=window)
+    ms = time_launches(fn, steps, warmup, torch)
+    npairs = window_pairs(N, window)
+    tf_alg = B * H * 8 * d * npairs / (ms * 1e-3) / 1e12
+    tf_exec = B * H * 12 * d * npairs / (ms * 1e-3) / 1e12
+    return {
+        "workload": "v1_swa_4k", "ms": ms, "value": round(tf_alg, 2), "unit": "TFLOP/s",
+        "config": {"workload": "v1_swa_4k", "B": B, "H": H, "N": N, "d": d, "dv": 2 * d,
+                   "window": window, "layer": layer, "dtype": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(tf_alg, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_alg / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("v1_swa_4k", "prefill"),
+                     "executed_mfma_tflops": round(tf_exec, 2),
+                     "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
+                     "kernel": "prefill_kernel<64,false,false> (sliding window)"},
+    }
+
+
 def bench_decode_v1(da, torch, steps, warmup):
     cfg, t = wl.make("v1_decode_32k")
     layer = cfg["layers"][0]
@@ -251,7 +282,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)  # clocks settle after ~20-50 ms of load
-    ap.add_argument("--only", choices=["v1", "v2", "decode", "decode_v1"], default=None)
+    ap.add_argument("--only", choices=["v1", "v2", "decode", "decode_v1", "swa"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -289,6 +320,10 @@ def main():
     if a.only in (None, "decode"):
         print("[bench] v2 decode", file=sys.stderr, flush=True)
         secondary.append(bench_decode(da, torch, a.steps, a.warmup))
+        torch.cuda.empty_cache()
+    if a.only in (None, "swa"):
+        print("[bench] v1 prefill, sliding window", file=sys.stderr, flush=True)
+        secondary.append(bench_swa(da, torch, a.steps, a.warmup))
         torch.cuda.empty_cache()
     if a.only in (None, "decode_v1"):
         print("[bench] v1 decode", file=sys.stderr, flush=True)

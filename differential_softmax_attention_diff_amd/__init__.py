@@ -10,6 +10,7 @@ GPU, the call fails.
 Entry points (same names as the C ABI):
   diffattn_fwd_v1(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer, ...)   V1 prefill
   diffattn_fwd_v2(q1, q2, k, v, lq1, lk1, lq2, lk2, layer, ...)        V2 prefill (GQA pairs)
+  (both take window=W for the causal sliding window: diffattn_fwd_v1_window / _v2_window)
   diffattn_decode(q1, q2, kcache, vcache, lq1, lk1, lq2, lk2, layer, ...)  V2 decode step
   diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits=0)
   diffattn_decode_v1(q1, q2, k1cache, k2cache, vcache, lq1, lk1, lq2, lk2, layer, ...)  V1 decode
@@ -76,6 +77,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.diffattn_fwd_v1.restype = i32
     lib.diffattn_fwd_v2.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp]
     lib.diffattn_fwd_v2.restype = i32
+    lib.diffattn_fwd_v1_window.argtypes = [T, T, T, T, T, T, i32, i32, i32, i32, i32, L, i32, f32, u32, vp]
+    lib.diffattn_fwd_v1_window.restype = i32
+    lib.diffattn_fwd_v2_window.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp]
+    lib.diffattn_fwd_v2_window.restype = i32
     lib.diffattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.diffattn_decode_workspace_bytes.restype = sz
     lib.diffattn_decode.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp, sz, vp]
@@ -191,12 +196,13 @@ def _check(status, where):
 # ------------------------------------------------------------------------------------------------
 
 def diffattn_fwd_v1(q1, q2, k1, k2, v, lq1=None, lk1=None, lq2=None, lk2=None, layer=1, *,
-                    out=None, causal=True, eps=1e-5, flags=0, lambda_override=None,
+                    out=None, causal=True, eps=1e-5, flags=0, window=0, lambda_override=None,
                     lambda_out=None, stream=None):
     """V1 differential attention; q1, q2, k1, k2 [B, H, N, d], v [B, H, N, 2d] -> out [B, H, N, 2d].
 
     bf16 tensors run the fused MFMA kernel, float32 tensors the fp32 kernel.  Lambda vectors are
-    float32 [H, d'] GPU tensors; ``layer`` is the 1-based layer of lambda_init.
+    float32 [H, d'] GPU tensors; ``layer`` is the 1-based layer of lambda_init.  ``window`` > 0
+    selects the causal sliding window (``diffattn_fwd_v1_window``).
     """
     torch = _torch()
     B, H, N, d = q1.shape
@@ -212,16 +218,25 @@ def diffattn_fwd_v1(q1, q2, k1, k2, v, lq1=None, lk1=None, lq2=None, lk2=None, l
     lam = _lambda(lq1, lk1, lq2, lk2, layer, H, lambda_override, lambda_out, q1.device)
     with torch.cuda.device(q1.device):
         st = _stream(q1.device, stream)
-        _check(load_library().diffattn_fwd_v1(*descs, B, H, N, d, dt, ctypes.byref(lam),
-                                              1 if causal else 0, float(eps), int(flags), st),
-               "diffattn_fwd_v1")
+        if window:
+            if not causal:
+                raise ValueError("the sliding window is a causal one")
+            _check(load_library().diffattn_fwd_v1_window(*descs, B, H, N, d, dt, ctypes.byref(lam),
+                                                         int(window), float(eps), int(flags), st),
+                   "diffattn_fwd_v1_window")
+        else:
+            _check(load_library().diffattn_fwd_v1(*descs, B, H, N, d, dt, ctypes.byref(lam),
+                                                  1 if causal else 0, float(eps), int(flags), st),
+                   "diffattn_fwd_v1")
     return out
 
 
 def diffattn_fwd_v2(q1, q2, k, v, lq1=None, lk1=None, lq2=None, lk2=None, layer=1, *,
-                    out=None, causal=True, lambda_override=None, lambda_out=None, stream=None):
+                    out=None, causal=True, window=0, lambda_override=None, lambda_out=None,
+                    stream=None):
     """V2 differential attention; q1, q2 [B, P, N, D] (query heads 2p and 2p+1), k, v [B, Hkv, N, D]
-    -> out [B, P, N, D].  Pair p reads KV head p * Hkv // P."""
+    -> out [B, P, N, D].  Pair p reads KV head p * Hkv // P.  ``window`` > 0 selects the causal
+    sliding window (``diffattn_fwd_v2_window``)."""
     torch = _torch()
     B, P, N, D = q1.shape
     Hkv = k.shape[1]
@@ -237,8 +252,15 @@ def diffattn_fwd_v2(q1, q2, k, v, lq1=None, lk1=None, lq2=None, lk2=None, layer=
     lam = _lambda(lq1, lk1, lq2, lk2, layer, P, lambda_override, lambda_out, q1.device)
     with torch.cuda.device(q1.device):
         st = _stream(q1.device, stream)
-        _check(load_library().diffattn_fwd_v2(*descs, B, P, Hkv, N, D, dt, ctypes.byref(lam),
-                                              1 if causal else 0, st), "diffattn_fwd_v2")
+        if window:
+            if not causal:
+                raise ValueError("the sliding window is a causal one")
+            _check(load_library().diffattn_fwd_v2_window(*descs, B, P, Hkv, N, D, dt,
+                                                         ctypes.byref(lam), int(window), st),
+                   "diffattn_fwd_v2_window")
+        else:
+            _check(load_library().diffattn_fwd_v2(*descs, B, P, Hkv, N, D, dt, ctypes.byref(lam),
+                                                  1 if causal else 0, st), "diffattn_fwd_v2")
     return out
 
 

@@ -99,11 +99,16 @@ const char* diffattn_status_string(da_status s) {
 
 const char* diffattn_version(void) { return "diffattn-gfx950 0.1.0"; }
 
-da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2, da_tensor v,
-                          da_tensor out, int32_t B, int32_t H, int32_t N, int32_t d,
-                          da_dtype dtype, const da_lambda* lam, int32_t causal, float eps,
-                          uint32_t flags, void* stream) {
-  if (B < 0 || H < 0 || N < 0) return DA_ERR_SHAPE;
+}  // extern "C"
+
+namespace {
+
+da_status fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2, da_tensor v,
+                 da_tensor out, int32_t B, int32_t H, int32_t N, int32_t d, da_dtype dtype,
+                 const da_lambda* lam, int32_t causal, int32_t window, float eps, uint32_t flags,
+                 void* stream) {
+  if (B < 0 || H < 0 || N < 0 || window < 0) return DA_ERR_SHAPE;
+  if (window > 0 && !causal) return DA_ERR_SHAPE;  // the window is a causal one
   if (B == 0 || H == 0 || N == 0) return DA_OK;
   if (dtype != DA_F32 && dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
   if (d != 64) return d <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
@@ -124,6 +129,7 @@ da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2
   p.sv = strides(v); p.so = strides(out);
   p.B = B; p.heads = H; p.Hkv = H; p.N = N;
   p.causal = causal ? 1 : 0;
+  p.window = window;
   p.norm = (flags & DA_V1_NO_NORM) ? 0 : 1;
   p.scale = (float)(1.0 / std::sqrt((double)d));
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
@@ -137,10 +143,11 @@ da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2
   return hip_status(da::launch_v1_bf16(p, st));
 }
 
-da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor out,
-                          int32_t B, int32_t P, int32_t Hkv, int32_t N, int32_t D,
-                          da_dtype dtype, const da_lambda* lam, int32_t causal, void* stream) {
-  if (B < 0 || P < 0 || Hkv < 0 || N < 0) return DA_ERR_SHAPE;
+da_status fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor out, int32_t B,
+                 int32_t P, int32_t Hkv, int32_t N, int32_t D, da_dtype dtype,
+                 const da_lambda* lam, int32_t causal, int32_t window, void* stream) {
+  if (B < 0 || P < 0 || Hkv < 0 || N < 0 || window < 0) return DA_ERR_SHAPE;
+  if (window > 0 && !causal) return DA_ERR_SHAPE;
   if (B == 0 || P == 0 || N == 0) return DA_OK;
   if (Hkv == 0) return DA_ERR_SHAPE;
   if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
@@ -162,6 +169,7 @@ da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, 
   p.sv = strides(v); p.so = strides(out);
   p.B = B; p.heads = P; p.Hkv = Hkv; p.N = N;
   p.causal = causal ? 1 : 0;
+  p.window = window;
   p.norm = 0;
   p.scale = (float)(1.0 / std::sqrt((double)D));
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
@@ -169,6 +177,39 @@ da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, 
   p.out_scale = 1.f;
   p.lam = lambda_args(lam);
   return hip_status(da::launch_v2_bf16(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2, da_tensor v,
+                          da_tensor out, int32_t B, int32_t H, int32_t N, int32_t d,
+                          da_dtype dtype, const da_lambda* lam, int32_t causal, float eps,
+                          uint32_t flags, void* stream) {
+  return fwd_v1(q1, q2, k1, k2, v, out, B, H, N, d, dtype, lam, causal, 0, eps, flags, stream);
+}
+
+da_status diffattn_fwd_v1_window(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2,
+                                 da_tensor v, da_tensor out, int32_t B, int32_t H, int32_t N,
+                                 int32_t d, da_dtype dtype, const da_lambda* lam, int32_t window,
+                                 float eps, uint32_t flags, void* stream) {
+  if (window < 1) return DA_ERR_SHAPE;
+  return fwd_v1(q1, q2, k1, k2, v, out, B, H, N, d, dtype, lam, 1, window, eps, flags, stream);
+}
+
+da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor out,
+                          int32_t B, int32_t P, int32_t Hkv, int32_t N, int32_t D,
+                          da_dtype dtype, const da_lambda* lam, int32_t causal, void* stream) {
+  return fwd_v2(q1, q2, k, v, out, B, P, Hkv, N, D, dtype, lam, causal, 0, stream);
+}
+
+da_status diffattn_fwd_v2_window(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v,
+                                 da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t N,
+                                 int32_t D, da_dtype dtype, const da_lambda* lam, int32_t window,
+                                 void* stream) {
+  if (window < 1) return DA_ERR_SHAPE;
+  return fwd_v2(q1, q2, k, v, out, B, P, Hkv, N, D, dtype, lam, 1, window, stream);
 }
 
 size_t diffattn_decode_workspace_bytes(int32_t B, int32_t P, int32_t Hkv, int32_t L, int32_t D,

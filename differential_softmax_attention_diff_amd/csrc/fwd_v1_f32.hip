@@ -59,11 +59,12 @@ __global__ __launch_bounds__(256) void v1_f32_kernel(const PrefillParams p) {
     q2r[e] = c.x; q2r[e + 1] = c.y; q2r[e + 2] = c.z; q2r[e + 3] = c.w;
   }
 
-  const int nk = p.causal ? i + 1 : p.N;  // visible keys: j < nk
+  const int nk = p.causal ? i + 1 : p.N;  // visible keys: j0 <= j < nk
+  const int jb = p.window > 0 ? max(0, i - p.window + 1) : 0;
 
   // sweep 1: row maxima of both branches
   float m1 = -INFINITY, m2 = -INFINITY;
-  for (int j0 = 0; j0 < nk; j0 += 64) {
+  for (int j0 = jb; j0 < nk; j0 += 64) {
     const int j = j0 + lane;
     if (j < nk) {
       m1 = fmaxf(m1, dot64(q1r, k1 + (int64_t)j * p.sk1.sn) * p.scale);
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void v1_f32_kernel(const PrefillParams p) {
   // sweep 2: exp(s - max), row sums, weighted value sums
   float l1 = 0.f, l2 = 0.f;
   float a1[2] = {0.f, 0.f}, a2[2] = {0.f, 0.f};
-  for (int j0 = 0; j0 < nk; j0 += 64) {
+  for (int j0 = jb; j0 < nk; j0 += 64) {
     const int j = j0 + lane;
     float e1 = 0.f, e2 = 0.f;
     if (j < nk) {

@@ -34,6 +34,7 @@ struct PrefillParams {
   Strides sq1, sq2, sk1, sk2, sv, so;
   int32_t B, heads, Hkv, N;
   int32_t causal;
+  int32_t window;        // causal sliding window: row i sees keys i-window+1 .. i (0: none)
   int32_t norm;          // V1: apply RMS norm + (1 - lambda_init) scale
   int32_t n_row_blocks;  // query row blocks per (batch, head group)
   int32_t pairs_per_kv;  // V2: P / Hkv

@@ -223,10 +223,14 @@ void prefill_kernel(const PrefillParams p) {
 
   const int kv_end = p.causal ? min(N, row0 + BM) : N;
   const int ntiles = (kv_end + kSBN - 1) / kSBN;
-  // tiles this wave computes: up to its last visible key
+  // sliding window: the block's first row sees keys from row0 - window + 1 on
+  const int t_begin = p.window > 0 ? max(0, row0 - p.window + 1) / kSBN : 0;
+  // tiles this wave computes: from the tile holding its first row's first visible key up to its
+  // last visible key
   const bool wave_has_rows = wrow < N;
   const int last_key = p.causal ? min(N, wrow + 32) : N;
   const int nt_wave = wave_has_rows ? min(ntiles, (last_key + kSBN - 1) / kSBN) : 0;
+  const int t0_wave = p.window > 0 ? max(t_begin, max(0, wrow - p.window + 1) / kSBN) : 0;
 
   const uint32_t k1_row = (uint32_t)(p.sk1.sn * 2), k2_row = (uint32_t)(p.sk2.sn * 2);
   const uint32_t v_row = (uint32_t)(p.sv.sn * 2);
@@ -365,12 +369,14 @@ void prefill_kernel(const PrefillParams p) {
   };
   // causal diagonal and ragged end only
   auto mask = [&](f32x16& s, int kt) {
-    if ((p.causal && kt + 31 > wrow) || kt + kSBN > N) {
+    const bool below = p.window > 0 && kt <= wrow + 31 - p.window;  // tile reaches below a window
+    if ((p.causal && kt + 31 > wrow) || kt + kSBN > N || below) {
       const int qrow = wrow + c;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kt + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (key >= N || (p.causal && key > qrow)) s[r] = -INFINITY;
+        if (key >= N || (p.causal && key > qrow) || (p.window > 0 && key <= qrow - p.window))
+          s[r] = -INFINITY;
       }
     }
   };
@@ -496,19 +502,30 @@ void prefill_kernel(const PrefillParams p) {
   };
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) {
-    if (i < ntiles) {
-      issue_tile(i);
-      if constexpr (F16PV) finish_v(i);
+    if (t_begin + i < ntiles) {
+      issue_tile(t_begin + i);
+      if constexpr (F16PV) finish_v((t_begin + i) % NS);
     }
   }
   if constexpr (NS == 2 || F16PV) {
     __builtin_amdgcn_s_waitcnt(0);
   } else {
-    if (ntiles > 1) __builtin_amdgcn_s_waitcnt(kLoadsPerTile | (7 << 4) | (15 << 8));
+    if (t_begin + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kLoadsPerTile | (7 << 4) | (15 << 8));
     else __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
-  int it = 0;
+  // tiles before this wave's window only need its share of the loads and the barriers
+  auto help = [&](int i) {
+    const int ahead = i + NS - 1;
+    if (ahead < ntiles) {
+      issue_tile(ahead);
+      if constexpr (F16PV) finish_v(ahead % NS);
+    }
+    wait_next(i);
+    __syncthreads();
+  };
+  int it = t_begin;
+  for (; it < t0_wave; ++it) help(it);
   for (; it < nt_wave; ++it) {
     if (tile_big(it)) break;
     step(it, std::false_type{});
@@ -516,15 +533,7 @@ void prefill_kernel(const PrefillParams p) {
   if constexpr (F16PV) {
     for (; it < nt_wave; ++it) step(it, std::true_type{});
   }
-  for (; it < ntiles; ++it) {
-    const int ahead = it + NS - 1;
-    if (ahead < ntiles) {
-      issue_tile(ahead);
-      if constexpr (F16PV) finish_v(ahead % NS);
-    }
-    wait_next(it);
-    __syncthreads();
-  }
+  for (; it < ntiles; ++it) help(it);
 
   // ---- epilogue: branch-2 waves publish lambda acc_2 / l_2; branch-1 waves finish the rows
   const float lam = head_lambda(p.lam, qh, lane);

@@ -113,6 +113,26 @@ da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, 
                           da_dtype dtype, const da_lambda* lam, int32_t causal, void* stream);
 
 /*
+ * diffattn_fwd_v1_window, diffattn_fwd_v2_window -- the same two layouts restricted to a causal
+ * sliding window, for the window layers of hybrid DIFF / sliding-window stacks
+ * (ai-engineering.academy "Atención Diferencial (V2)", section "Úselo").  Query row i sees keys
+ * i - window + 1 .. i (its last `window` positions, itself included); window >= N is plain
+ * causal.  Arguments, layouts and results are those of diffattn_fwd_v1 / diffattn_fwd_v2 with
+ * causal = 1, and:
+ *   window : >= 1 (DA_ERR_SHAPE otherwise).
+ * A decode step over a window needs no entry point of its own: pass the last `window` cache
+ * rows (a strided view) to diffattn_decode / diffattn_decode_v1.
+ */
+da_status diffattn_fwd_v1_window(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2,
+                                 da_tensor v, da_tensor out, int32_t B, int32_t H, int32_t N,
+                                 int32_t d, da_dtype dtype, const da_lambda* lam, int32_t window,
+                                 float eps, uint32_t flags, void* stream);
+da_status diffattn_fwd_v2_window(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v,
+                                 da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t N,
+                                 int32_t D, da_dtype dtype, const da_lambda* lam, int32_t window,
+                                 void* stream);
+
+/*
  * Bytes of device workspace diffattn_decode needs for these sizes and split count
  * (num_splits <= 0 selects the library's default).  Returns 0 for unsupported sizes.
  */

@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_header_symbols_exported(da):
     names = _declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -161,6 +161,34 @@ def test_decode_v1_workspace_size_formula(da):
     assert da.diffattn_decode_v1_workspace_bytes(1, 1, 100, 64, 0) == 1 * 2 * 1 * 130 * 4
     assert da.diffattn_decode_v1_workspace_bytes(1, 1, 1000, 64, 3) == 2 * 2 * 130 * 4
     assert da.diffattn_decode_v1_workspace_bytes(32, 16, 32768, 64, 0) == 32 * 16 * 2 * 8 * 130 * 4
+
+
+def test_window_host_validation(da):
+    lib = da.load_library()
+    t6 = [_t() for _ in range(6)]
+    lam = _lam()
+    w1 = lambda window, B=1, H=1, N=8: lib.diffattn_fwd_v1_window(
+        *t6, B, H, N, 64, 1, ctypes.byref(lam), window, 1e-5, 0, None)
+    assert w1(0) == 2                      # the window needs at least one key
+    assert w1(-3) == 2
+    assert w1(4, B=0) == 0
+    t5 = [_t() for _ in range(5)]
+    lam2 = _lam(dl=128)
+    w2 = lambda window, P=4, Hkv=2: lib.diffattn_fwd_v2_window(
+        *t5, 1, P, Hkv, 8, 128, 1, ctypes.byref(lam2), window, None)
+    assert w2(0) == 2
+    assert w2(5, P=3) == 2                 # P % Hkv
+    # the causal entry points reject nothing new
+    assert _v1(lib, t6, N=0) == 0
+
+
+def test_binding_window_requires_causal(da):
+    import torch
+
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    v = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        da.diffattn_fwd_v1(x, x, x, x, v, layer=1, out=v, causal=False, window=4)
 
 
 def test_binding_refuses_cpu_tensors(da):

@@ -16,8 +16,9 @@ Workloads
 ---------
 ``CONFIGS`` lists the workloads: a small fp32 V1 case, the V1 prefill at a 4K context, the V2
 (GQA, paired query heads) prefill at 8K, the V2 decode step over a 32K-token cache, the V1
-long-context prefill at 128K tokens with planted "needle" keys, and the V1-layout decode step
-over a 32K-token cache (its K1 + K2 + V cache is as large as the V2 decode's K + V cache).
+long-context prefill at 128K tokens with planted "needle" keys, the V1-layout decode step
+over a 32K-token cache (its K1 + K2 + V cache is as large as the V2 decode's K + V cache), and
+the V1 prefill at 4K restricted to a causal sliding window of 1024 keys.
 """
 
 from __future__ import annotations
@@ -44,6 +45,8 @@ CONFIGS = {
                          layers=tuple(range(1, 33)), eps=1e-5, needles=6, seed=1005),
     "v1_decode_32k": dict(kind="decode_v1", dtype="bf16", B=32, H=16, L=32768, d=64,
                           layers=(12,), eps=1e-5, seed=1006),
+    "v1_swa_4k": dict(kind="v1", dtype="bf16", B=4, H=16, N=4096, d=64, causal=True, window=1024,
+                      layers=(12,), eps=1e-5, seed=1007),
 }
 
 _TAGS = {"q1": 1, "q2": 2, "k1": 3, "k2": 4, "v": 5, "q": 6, "k": 7,
