@@ -208,6 +208,41 @@ def bench_swa(da, torch, steps, warmup):
     }
 
 
+def bench_decode_paged(da, torch, steps, warmup):
+    cfg, t = wl.make("v2_decode_paged")
+    layer = cfg["layers"][0]
+    B, P, Hkv, D, ps = cfg["B"], cfg["P"], cfg["Hkv"], cfg["D"], cfg["page_size"]
+    q = to_dev(t["q"], torch)
+    kp, vp = to_dev(t["k_pages"], torch), to_dev(t["v_pages"], torch)
+    del t["k_pages"], t["v_pages"]
+    bt = torch.from_numpy(t["block_table"]).to("cuda")
+    sl = torch.from_numpy(t["seq_lens"]).to("cuda")
+    max_len = int(t["seq_lens"].max())
+    lv = [torch.from_numpy(x).to("cuda") for x in t["lambda"][layer]]
+    out = torch.empty((B, P, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(da.diffattn_decode_workspace_bytes(B, P, Hkv, max_len, D), dtype=torch.uint8,
+                     device="cuda")
+    q1, q2 = q[:, 0::2], q[:, 1::2]
+    fn = lambda: da.diffattn_decode_paged(q1, q2, kp, vp, bt, sl, *lv, layer=layer, max_len=max_len,
+                                          out=out, workspace=ws)
+    ms = time_launches(fn, steps, warmup, torch)
+    keys = int(t["seq_lens"].sum())
+    # every live key's K and V rows once, the block table, q and out
+    nbytes = 2 * keys * Hkv * D * 2 + t["block_table"].nbytes + B * 2 * P * D * 2 + B * P * D * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": "v2_decode_paged", "ms": ms, "value": round(gbs, 1), "unit": "GB/s",
+        "config": {"workload": "v2_decode_paged", "B": B, "P": P, "query_heads": 2 * P, "Hkv": Hkv,
+                   "D": D, "page_size": ps, "seq_len_range": [cfg["len_lo"], cfg["len_hi"]],
+                   "total_keys": keys, "layer": layer, "dtype": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("v2_decode_paged", "decode"),
+                     "algorithmic_bytes": nbytes,
+                     "kernel": "decode_partial_kernel<4,true> + decode_combine_kernel (whole step)"},
+    }
+
+
 def bench_decode_v1(da, torch, steps, warmup):
     cfg, t = wl.make("v1_decode_32k")
     layer = cfg["layers"][0]
@@ -282,7 +317,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)  # clocks settle after ~20-50 ms of load
-    ap.add_argument("--only", choices=["v1", "v2", "decode", "decode_v1", "swa"], default=None)
+    ap.add_argument("--only", choices=["v1", "v2", "decode", "decode_v1", "swa", "paged"],
+                    default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -320,6 +356,10 @@ def main():
     if a.only in (None, "decode"):
         print("[bench] v2 decode", file=sys.stderr, flush=True)
         secondary.append(bench_decode(da, torch, a.steps, a.warmup))
+        torch.cuda.empty_cache()
+    if a.only in (None, "paged"):
+        print("[bench] v2 decode, paged cache", file=sys.stderr, flush=True)
+        secondary.append(bench_decode_paged(da, torch, a.steps, a.warmup))
         torch.cuda.empty_cache()
     if a.only in (None, "swa"):
         print("[bench] v1 prefill, sliding window", file=sys.stderr, flush=True)

@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
   (both take window=W for the causal sliding window: diffattn_fwd_v1_window / _v2_window)
   diffattn_decode(q1, q2, kcache, vcache, lq1, lk1, lq2, lk2, layer, ...)  V2 decode step
   diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits=0)
+  diffattn_decode_paged(q1, q2, k_pages, v_pages, block_table, seq_lens, lq1, ...)  V2 decode,
+      paged KV cache with per-sequence lengths
   diffattn_decode_v1(q1, q2, k1cache, k2cache, vcache, lq1, lk1, lq2, lk2, layer, ...)  V1 decode
   diffattn_decode_v1_workspace_bytes(B, H, L, d, num_splits=0)
   diffattn_lambda_init(layer)
@@ -27,6 +29,7 @@ __all__ = [
     "DiffAttnError", "load_library", "LIB_PATH",
     "DA_F32", "DA_BF16", "DA_V1_NO_NORM",
     "diffattn_fwd_v1", "diffattn_fwd_v2", "diffattn_decode", "diffattn_decode_v1",
+    "diffattn_decode_paged",
     "diffattn_decode_workspace_bytes", "diffattn_decode_v1_workspace_bytes", "diffattn_lambda_init",
     "diffattn_status_string", "diffattn_version",
 ]
@@ -85,6 +88,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.diffattn_decode_workspace_bytes.restype = sz
     lib.diffattn_decode.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp, sz, vp]
     lib.diffattn_decode.restype = i32
+    lib.diffattn_decode_paged.argtypes = [T, T, vp, vp, vp, vp, T, i32, i32, i32, i32, i32, i32, i32,
+                                          i32, i32, L, i32, vp, sz, vp]
+    lib.diffattn_decode_paged.restype = i32
     lib.diffattn_decode_v1_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.diffattn_decode_v1_workspace_bytes.restype = sz
     lib.diffattn_decode_v1.argtypes = [T, T, T, T, T, T, i32, i32, i32, i32, i32, L, f32, u32, i32,
@@ -334,4 +340,47 @@ def diffattn_decode_v1(q1, q2, k1cache, k2cache, vcache, lq1=None, lk1=None, lq2
                                                  float(eps), int(flags), int(num_splits),
                                                  workspace.data_ptr(), ws_bytes, st),
                "diffattn_decode_v1")
+    return out
+
+
+def diffattn_decode_paged(q1, q2, k_pages, v_pages, block_table, seq_lens, lq1=None, lk1=None,
+                          lq2=None, lk2=None, layer=1, *, max_len=None, out=None, num_splits=0,
+                          workspace=None, lambda_override=None, lambda_out=None, stream=None):
+    """One V2 decode step on a paged KV cache; q1, q2 [B, P, D]; k_pages, v_pages
+    [num_pages, Hkv, page_size, D] (contiguous); block_table int32 [B, max_blocks]; seq_lens
+    int32 [B] -> out [B, P, D].  ``max_len`` bounds seq_lens (default max_blocks * page_size)."""
+    torch = _torch()
+    B, P, D = q1.shape
+    num_pages, Hkv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    max_blocks = block_table.shape[1]
+    if max_len is None:
+        max_len = max_blocks * page_size
+    if out is None:
+        out = torch.empty((B, P, D), dtype=q1.dtype, device=q1.device)
+    dt = _dtype_code(q1)
+    for nm, x in (("q2", q2), ("k_pages", k_pages), ("v_pages", v_pages), ("out", out)):
+        if x.dtype != q1.dtype:
+            raise TypeError(f"{nm} dtype {x.dtype} differs from q1 dtype {q1.dtype}")
+    for nm, x, shape in (("k_pages", k_pages, (num_pages, Hkv, page_size, D)),
+                         ("v_pages", v_pages, (num_pages, Hkv, page_size, D))):
+        if tuple(x.shape) != shape or not x.is_contiguous() or not x.is_cuda:
+            raise ValueError(f"{nm} must be a contiguous GPU tensor of shape {shape}")
+    for nm, x, shape in (("block_table", block_table, (B, max_blocks)), ("seq_lens", seq_lens, (B,))):
+        if x.dtype != torch.int32 or tuple(x.shape) != shape or not x.is_contiguous() or not x.is_cuda:
+            raise ValueError(f"{nm} must be a contiguous int32 GPU tensor of shape {shape}")
+    descs = [_desc(q1, "q1", (B, P, D)), _desc(q2, "q2", (B, P, D))]
+    need = diffattn_decode_workspace_bytes(B, P, Hkv, max_len, D, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lam = _lambda(lq1, lk1, lq2, lk2, layer, P, lambda_override, lambda_out, q1.device)
+    with torch.cuda.device(q1.device):
+        st = _stream(q1.device, stream)
+        _check(load_library().diffattn_decode_paged(
+            *descs, k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+            seq_lens.data_ptr(), _desc(out, "out", (B, P, D)), B, P, Hkv, D, page_size, num_pages,
+            max_blocks, int(max_len), dt, ctypes.byref(lam), int(num_splits), workspace.data_ptr(),
+            ws_bytes, st), "diffattn_decode_paged")
     return out

@@ -257,6 +257,59 @@ da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tenso
   return hip_status(da::launch_decode_v2(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
+da_status diffattn_decode_paged(da_tensor q1, da_tensor q2, const void* k_pages,
+                                const void* v_pages, const int32_t* block_table,
+                                const int32_t* seq_lens, da_tensor out, int32_t B, int32_t P,
+                                int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                int32_t max_blocks, int32_t max_len, da_dtype dtype,
+                                const da_lambda* lam, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (B < 0 || P < 0 || Hkv < 0) return DA_ERR_SHAPE;
+  if (B == 0 || P == 0) return DA_OK;
+  if (Hkv == 0 || max_len < 1 || num_pages < 1 || max_blocks < 1) return DA_ERR_SHAPE;
+  if (page_size < 1 || page_size > (1 << 16) || (page_size & (page_size - 1)) != 0) return DA_ERR_SHAPE;
+  if ((int64_t)max_blocks * page_size < max_len) return DA_ERR_SHAPE;
+  if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
+  if (D != 128) return D <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+  if (P % Hkv != 0) return DA_ERR_SHAPE;
+  const int G = 2 * P / Hkv;
+  if (G != 2 && G != 4 && G != 8 && G != 16) return DA_ERR_UNSUPPORTED;
+  if (B > kMaxGridY || Hkv > kMaxGridY || P > INT32_MAX / 2) return DA_ERR_UNSUPPORTED;
+  for (const da_tensor* t : {&q1, &q2, &out}) {
+    const da_status s = check_tensor(*t, 2);
+    if (s != DA_OK) return s;
+  }
+  if (!k_pages || !v_pages || !aligned16(k_pages) || !aligned16(v_pages)) return DA_ERR_NULL;
+  if (!block_table || !seq_lens || (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0)
+    return DA_ERR_NULL;
+  da_status s = check_lambda(lam, 256);
+  if (s != DA_OK) return s;
+  const size_t need = diffattn_decode_workspace_bytes(B, P, Hkv, max_len, D, num_splits);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return DA_ERR_WORKSPACE;
+
+  da::DecodeParams p{};
+  p.q1 = q1.ptr; p.q2 = q2.ptr; p.k = k_pages; p.v = v_pages; p.out = out.ptr;
+  p.sq1 = strides(q1); p.sq2 = strides(q2); p.so = strides(out);
+  p.sk = da::Strides{0, 0, 0}; p.sv = da::Strides{0, 0, 0};
+  p.B = B; p.P = P; p.Hkv = Hkv; p.L = max_len; p.D = D;
+  p.chunk = decode_chunk(B, Hkv, max_len, num_splits);
+  p.splits = (max_len + p.chunk - 1) / p.chunk;
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  const int64_t n_rows = (int64_t)B * 2 * P * p.splits;
+  p.ws_acc = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_acc + n_rows * D;
+  p.lam = lambda_args(lam);
+  p.block_table = block_table;
+  p.seq_lens = seq_lens;
+  p.max_blocks = max_blocks;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  p.page_shift = shift;
+  p.num_pages = num_pages;
+  return hip_status(da::launch_decode_v2_paged(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t diffattn_decode_v1_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d,
                                           int32_t num_splits) {
   if (B <= 0 || H <= 0 || L <= 0 || d != 64) return 0;

@@ -28,14 +28,17 @@ constexpr int kKB = 256;  // keys per block (64 per wavefront)
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;
 
-// G = query heads per KV head (2P / Hkv): 2, 4, 8 or 16.
-template <int G>
+// G = query heads per KV head (2P / Hkv): 2, 4, 8 or 16.  PAGED: the cache is a pool of pages
+// [num_pages, Hkv, page_size, D] addressed through a per-sequence block table, and every sequence
+// has its own length (the serving layout); otherwise [B, Hkv, L, D] with strides and one length.
+template <int G, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
   constexpr int SLOTS = (G + 3) / 4;  // heads whose softmax state one wavefront owns
   __shared__ float sc_lds[G][kKB];    // scores of the block, per head
   __shared__ __attribute__((aligned(16))) float pw_lds[kKB][G];  // exp-weights, per key
   __shared__ float alpha_lds[G];
   __shared__ float red_lds[4][G][kD];
+  __shared__ int tab_lds[PAGED ? 2 : 1][PAGED ? kKB : 1];  // page of each page-sized run of a block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -46,12 +49,42 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
   const int l16 = lane & 15;
   const int grp = lane >> 4;
 
-  const int k_begin = split * p.chunk;
-  const int k_end = min(p.L, k_begin + p.chunk);
+  // keys of this sequence (paged: its own length, clamped to the table's extent)
+  const int seq_len = PAGED ? min(max(p.seq_lens[b], 0), min(p.L, p.max_blocks << p.page_shift)) : p.L;
+  // the sequence's 256-key blocks are dealt evenly to the splits, so that with per-sequence
+  // lengths every split of a sequence gets the same share (empty only when it has fewer blocks
+  // than splits)
+  const int nblk = (seq_len + kKB - 1) / kKB;
+  const int k_begin = (int)(((int64_t)split * nblk) / p.splits) * kKB;
+  const int k_end = min(seq_len, (int)(((int64_t)(split + 1) * nblk) / p.splits) * kKB);
   const float c2 = p.scale_log2;
 
   const bf16* kbase = static_cast<const bf16*>(p.k) + b * p.sk.sb + g * p.sk.sh;
   const bf16* vbase = static_cast<const bf16*>(p.v) + b * p.sv.sb + g * p.sv.sh;
+  // Paged: the page indices of a block's keys are staged in LDS one block ahead (a block of 256
+  // keys starts on a multiple of 256, so it spans 256 / page_size pages, or lies inside one).
+  // A page index outside the pool is clamped, so that a bad table entry cannot address memory
+  // beyond it.
+  const int32_t* btab = PAGED ? p.block_table + (int64_t)b * p.max_blocks : nullptr;
+  const int page_mask = (1 << p.page_shift) - 1;
+  const int tab_n = p.page_shift >= 8 ? 1 : kKB >> p.page_shift;  // pages per block
+  auto fetch_tab = [&](int blk) -> int {  // this thread's entry for the block starting at blk
+    const int e = (blk >> p.page_shift) + tid;
+    return (tid < tab_n && e < p.max_blocks) ? min(max(btab[e], 0), p.num_pages - 1) : 0;
+  };
+  int cur = 0;
+  auto row = [&](int key, int blk, int64_t sn) -> int64_t {
+    if constexpr (PAGED) {
+      const int pg = tab_lds[cur][(key >> p.page_shift) - (blk >> p.page_shift)];
+      return (((int64_t)pg * p.Hkv + g) << p.page_shift | (key & page_mask)) * kD;
+    } else {
+      return (int64_t)key * sn;
+    }
+  };
+  if constexpr (PAGED) {
+    if (k_begin < k_end) tab_lds[0][tid] = fetch_tab(k_begin);
+    __syncthreads();
+  }
 
   // A operand: row m = l16 is query head g*G + l16 (zero rows beyond G); k = 32t + 8*grp + i
   bf16x8 qa[4];
@@ -81,6 +114,11 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
   for (int blk = k_begin; blk < k_end; blk += kKB) {
+    // paged: the next block's page indices are loaded now and published at the end of the block
+    int tab_next = 0;
+    if constexpr (PAGED) {
+      if (blk + kKB < k_end) tab_next = fetch_tab(blk + kKB);
+    }
     // issue this block's K and V loads up front
     u32x4 kf[4][4];
 #pragma unroll
@@ -88,14 +126,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
       const int key = blk + 64 * w + 16 * sb + l16;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        kf[sb][t] = key < k_end ? load16(kbase + (int64_t)key * p.sk.sn + 32 * t + 8 * grp)
+        kf[sb][t] = key < k_end ? load16(kbase + row(key, blk, p.sk.sn) + 32 * t + 8 * grp)
                                 : u32x4{0u, 0u, 0u, 0u};
     }
     u32x4 vf[16];
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
       const int key = blk + 64 * w + 4 * st + grp;
-      vf[st] = key < k_end ? load16(vbase + (int64_t)key * p.sv.sn + 8 * l16) : u32x4{0u, 0u, 0u, 0u};
+      vf[st] = key < k_end ? load16(vbase + row(key, blk, p.sv.sn) + 8 * l16) : u32x4{0u, 0u, 0u, 0u};
     }
 
     // scores: D[m = head 4*grp + r][n = key l16] for 16 keys per MFMA group
@@ -175,6 +213,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
           for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pw[r], vv[e], acc[r][e]);
       }
     }
+    if constexpr (PAGED) {
+      tab_lds[cur ^ 1][tid] = tab_next;
+      cur ^= 1;
+    }
     __syncthreads();
   }
 
@@ -244,28 +286,37 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(const DecodeParams p
   out[ch] = (bf16)(o[0] - lam * o[1]);
 }
 
-template <int G>
+template <int G, bool PAGED>
 hipError_t launch_partial(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.splits, p.Hkv, p.B);
-  hipLaunchKernelGGL(decode_partial_kernel<G>, grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_partial_kernel<G, PAGED>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t launch_step(const DecodeParams& p, hipStream_t stream) {
+  const int G = 2 * p.P / p.Hkv;
+  hipError_t e;
+  switch (G) {
+    case 2: e = launch_partial<2, PAGED>(p, stream); break;
+    case 4: e = launch_partial<4, PAGED>(p, stream); break;
+    case 8: e = launch_partial<8, PAGED>(p, stream); break;
+    case 16: e = launch_partial<16, PAGED>(p, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.P, p.B), dim3(kD), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_v2(const DecodeParams& p, hipStream_t stream) {
-  const int G = 2 * p.P / p.Hkv;
-  hipError_t e;
-  switch (G) {
-    case 2: e = launch_partial<2>(p, stream); break;
-    case 4: e = launch_partial<4>(p, stream); break;
-    case 8: e = launch_partial<8>(p, stream); break;
-    case 16: e = launch_partial<16>(p, stream); break;
-    default: return hipErrorInvalidValue;
-  }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(p.P, p.B), dim3(kD), 0, stream, p);
-  return hipGetLastError();
+  return launch_step<false>(p, stream);
+}
+
+hipError_t launch_decode_v2_paged(const DecodeParams& p, hipStream_t stream) {
+  return launch_step<true>(p, stream);
 }
 
 }  // namespace da

@@ -60,6 +60,12 @@ struct DecodeParams {
   float* ws_acc;         // [B, 2P, splits, D]
   float* ws_ml;          // [B, 2P, splits, 2]  (running max in score units, sum)
   LambdaArgs lam;
+  // Paged cache (serving layout); k / v then point at pages [num_pages, Hkv, page_size, D].
+  const int32_t* block_table;  // [B, max_blocks] page index of each page_size-key block
+  const int32_t* seq_lens;     // [B] keys of each sequence (1 .. L; L is the longest)
+  int32_t max_blocks;
+  int32_t page_shift;          // log2(page_size)
+  int32_t num_pages;
 };
 
 // One V1 decode step: split-K partial pass + combine pass (norm and scale in the combine).

@@ -159,6 +159,35 @@ da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tenso
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * diffattn_decode_paged -- the V2 decode step on the serving layout: a pool of KV pages addressed
+ * through a per-sequence block table, each sequence with its own length (the layout of the
+ * production inference servers that ai-engineering.academy "Atención Diferencial (V2)", section
+ * "Úselo", names for V2).  Same computation as diffattn_decode with L = seq_lens[b] for
+ * sequence b (its own K/V sits at row seq_lens[b] - 1).
+ *
+ *   q1, q2 : [B, P, D]  (3-D: sb, sh used, sn ignored)            out : [B, P, D]
+ *   k_pages, v_pages : contiguous [num_pages, Hkv, page_size, D] bf16, 16-byte aligned
+ *   block_table : contiguous int32 [B, max_blocks]; key j of sequence b lives in page
+ *                 block_table[b][j / page_size], row j % page_size
+ *   seq_lens    : int32 [B], each in 1 .. max_len (device data: not checked on the host; values
+ *                 are clamped to [0, max_len] and page indices to [0, num_pages), so a bad entry
+ *                 gives wrong values but no access outside the buffers; a length of 0 gives NaN)
+ *   max_len     : host-side bound on seq_lens (<= max_blocks * page_size); sizes the split-K
+ *                 grid and the workspace, diffattn_decode_workspace_bytes(B, P, Hkv, max_len, D,
+ *                 num_splits) bytes.
+ *   page_size   : a power of two, 1 .. 65536.
+ *
+ * Supported: D == 128, dtype DA_BF16, P % Hkv == 0, 2P / Hkv <= 16.
+ */
+da_status diffattn_decode_paged(da_tensor q1, da_tensor q2, const void* k_pages,
+                                const void* v_pages, const int32_t* block_table,
+                                const int32_t* seq_lens, da_tensor out, int32_t B, int32_t P,
+                                int32_t Hkv, int32_t D, int32_t page_size, int32_t num_pages,
+                                int32_t max_blocks, int32_t max_len, da_dtype dtype,
+                                const da_lambda* lam, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace diffattn_decode_v1 needs for these sizes and split count
  * (num_splits <= 0 selects the library's default).  Returns 0 for unsupported sizes.
  */

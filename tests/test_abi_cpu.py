@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_header_symbols_exported(da):
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -189,6 +189,30 @@ def test_binding_window_requires_causal(da):
     v = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         da.diffattn_fwd_v1(x, x, x, x, v, layer=1, out=v, causal=False, window=4)
+
+
+def test_paged_decode_host_validation(da):
+    lib = da.load_library()
+    t3 = [_t() for _ in range(3)]
+    lam = _lam(dl=128)
+    need = da.diffattn_decode_workspace_bytes(2, 4, 2, 1000, 128)
+    call = lambda page=16, pages=100, mb=64, ml=1000, P=4, Hkv=2, D=128, ws=0x30000, nbytes=need, \
+        kp=0x40000, bt=0x50000: lib.diffattn_decode_paged(
+            t3[0], t3[1], kp, 0x40000, bt, 0x60000, t3[2], 2, P, Hkv, D, page, pages, mb, ml, 1,
+            ctypes.byref(lam), 0, ws, nbytes, None)
+    assert call(page=12) == 2            # not a power of two
+    assert call(page=0) == 2
+    assert call(ml=0) == 2
+    assert call(mb=10) == 2              # 10 pages of 16 keys cannot hold 1000
+    assert call(pages=0) == 2
+    assert call(D=64) == 3
+    assert call(P=3) == 2
+    assert call(P=16, Hkv=1) == 3        # 32 query heads on one KV head
+    assert call(kp=0x40008) == 1         # misaligned page pool
+    assert call(kp=0) == 1
+    assert call(bt=0x50002) == 1         # misaligned block table
+    assert call(ws=None) == 4
+    assert call(nbytes=need - 1) == 4
 
 
 def test_binding_refuses_cpu_tensors(da):

@@ -18,7 +18,8 @@ Workloads
 (GQA, paired query heads) prefill at 8K, the V2 decode step over a 32K-token cache, the V1
 long-context prefill at 128K tokens with planted "needle" keys, the V1-layout decode step
 over a 32K-token cache (its K1 + K2 + V cache is as large as the V2 decode's K + V cache), and
-the V1 prefill at 4K restricted to a causal sliding window of 1024 keys.
+the V1 prefill at 4K restricted to a causal sliding window of 1024 keys, and the V2 decode step
+on a paged KV cache (16-key pages in a random order, per-sequence lengths 4K .. 32K).
 """
 
 from __future__ import annotations
@@ -47,6 +48,8 @@ CONFIGS = {
                           layers=(12,), eps=1e-5, seed=1006),
     "v1_swa_4k": dict(kind="v1", dtype="bf16", B=4, H=16, N=4096, d=64, causal=True, window=1024,
                       layers=(12,), eps=1e-5, seed=1007),
+    "v2_decode_paged": dict(kind="decode_paged", dtype="bf16", B=64, P=16, Hkv=8, D=128,
+                            page_size=16, len_lo=4096, len_hi=32768, layers=(24,), seed=1008),
 }
 
 _TAGS = {"q1": 1, "q2": 2, "k1": 3, "k2": 4, "v": 5, "q": 6, "k": 7,
@@ -196,6 +199,36 @@ def make_decode_v1(B, H, L, d, dtype="bf16", seed=0, layers=(1,)):
     }
 
 
+def make_decode_paged(B, P, Hkv, D, page_size, seq_lens, dtype="bf16", seed=0, layers=(1,)):
+    """V2 decode inputs in the serving layout: q [B, 2P, D]; a pool of KV pages
+    [num_pages, Hkv, page_size, D]; block_table [B, max_blocks] (pages dealt in a seeded random
+    order, unused entries -1); seq_lens [B].  Every page of the pool is drawn N(0, 1)."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    blocks = [(int(n) + page_size - 1) // page_size for n in seq_lens]
+    num_pages = int(sum(blocks))
+    max_blocks = max(blocks)
+    order = _stream(seed, "needle", 0, 0).permutation(num_pages).astype(np.int32)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    pos = 0
+    for b, nb in enumerate(blocks):
+        table[b, :nb] = order[pos:pos + nb]
+        pos += nb
+    q = normal_tensor(seed, "q", (B, 2 * P, 1, D), dtype)[:, :, 0, :].copy()
+    return {
+        "q": q,
+        "k_pages": normal_tensor(seed, "k", (num_pages, Hkv, page_size, D), dtype),
+        "v_pages": normal_tensor(seed, "v", (num_pages, Hkv, page_size, D), dtype),
+        "block_table": table,
+        "seq_lens": seq_lens,
+        "lambda": {l: lambda_vectors(seed, P, D, l) for l in layers},
+    }
+
+
+def paged_lens(B, lo, hi, seed):
+    """Seeded per-sequence lengths, uniform in [lo, hi]."""
+    return _stream(seed, "needle", 1, 0).integers(lo, hi + 1, size=B).astype(np.int32)
+
+
 def make(name: str, **overrides):
     """Inputs of a named workload (``CONFIGS``), with optional shape overrides."""
     cfg = dict(CONFIGS[name])
@@ -210,6 +243,10 @@ def make(name: str, **overrides):
     if kind == "decode":
         return cfg, make_decode(cfg["B"], cfg["P"], cfg["Hkv"], cfg["L"], cfg["D"], cfg["dtype"],
                                 cfg["seed"], cfg["layers"])
+    if kind == "decode_paged":
+        lens = paged_lens(cfg["B"], cfg["len_lo"], cfg["len_hi"], cfg["seed"])
+        return cfg, make_decode_paged(cfg["B"], cfg["P"], cfg["Hkv"], cfg["D"], cfg["page_size"], lens,
+                                      cfg["dtype"], cfg["seed"], cfg["layers"])
     if kind == "decode_v1":
         return cfg, make_decode_v1(cfg["B"], cfg["H"], cfg["L"], cfg["d"], cfg["dtype"], cfg["seed"],
                                    cfg["layers"])
