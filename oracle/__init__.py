@@ -10,6 +10,7 @@ Contents
 ``diffattn_oracle``  plain numpy float64 implementation of the method's definition
 ``bruteforce``       an independent pure-Python (lists + ``math.exp``) version for tiny inputs
 ``compare``          the parity metrics and tolerances the tests apply
+``diffattn_backward`` float64 gradients of the V1 layout (chain rule on the definition)
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against values the source
 pages print, closed forms, special cases that reduce to library routines and brute force.
@@ -30,3 +31,4 @@ from .diffattn_oracle import (  # noqa: F401
     diff_decode_v2,
     diff_decode_v1,
 )
+from .diffattn_backward import diff_attn_v1_backward  # noqa: F401,E402
