@@ -17,6 +17,7 @@ Entry points (same names as the C ABI):
       paged KV cache with per-sequence lengths
   diffattn_decode_v1(q1, q2, k1cache, k2cache, vcache, lq1, lk1, lq2, lk2, layer, ...)  V1 decode
   diffattn_decode_v1_workspace_bytes(B, H, L, d, num_splits=0)
+  diffattn_fwd_v1_train(...), diffattn_bwd_v1(...)   V1 training forward (with stash) and backward
   diffattn_lambda_init(layer)
 """
 
@@ -29,7 +30,8 @@ __all__ = [
     "DiffAttnError", "load_library", "LIB_PATH",
     "DA_F32", "DA_BF16", "DA_V1_NO_NORM",
     "diffattn_fwd_v1", "diffattn_fwd_v2", "diffattn_decode", "diffattn_decode_v1",
-    "diffattn_decode_paged",
+    "diffattn_decode_paged", "diffattn_fwd_v1_train", "diffattn_bwd_v1",
+    "diffattn_v1_train_stash_bytes", "diffattn_bwd_v1_workspace_bytes",
     "diffattn_decode_workspace_bytes", "diffattn_decode_v1_workspace_bytes", "diffattn_lambda_init",
     "diffattn_status_string", "diffattn_version",
 ]
@@ -53,6 +55,11 @@ class DaLambda(ctypes.Structure):
     _fields_ = [("lq1", ctypes.c_void_p), ("lk1", ctypes.c_void_p), ("lq2", ctypes.c_void_p),
                 ("lk2", ctypes.c_void_p), ("dl", ctypes.c_int32), ("layer", ctypes.c_int32),
                 ("lambda_override", ctypes.c_void_p), ("lambda_out", ctypes.c_void_p)]
+
+
+class DaLambdaGrad(ctypes.Structure):
+    _fields_ = [("dlq1", ctypes.c_void_p), ("dlk1", ctypes.c_void_p), ("dlq2", ctypes.c_void_p),
+                ("dlk2", ctypes.c_void_p)]
 
 
 class DiffAttnError(RuntimeError):
@@ -91,6 +98,15 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.diffattn_decode_paged.argtypes = [T, T, vp, vp, vp, vp, T, i32, i32, i32, i32, i32, i32, i32,
                                           i32, i32, L, i32, vp, sz, vp]
     lib.diffattn_decode_paged.restype = i32
+    lib.diffattn_v1_train_stash_bytes.argtypes = [i32, i32, i32, i32]
+    lib.diffattn_v1_train_stash_bytes.restype = sz
+    lib.diffattn_bwd_v1_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.diffattn_bwd_v1_workspace_bytes.restype = sz
+    lib.diffattn_fwd_v1_train.argtypes = [T, T, T, T, T, T, i32, i32, i32, i32, i32, L, i32, f32, vp, sz, vp]
+    lib.diffattn_fwd_v1_train.restype = i32
+    lib.diffattn_bwd_v1.argtypes = [T, T, T, T, T, T, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, L,
+                                    ctypes.POINTER(DaLambdaGrad), i32, f32, vp, sz, vp, sz, vp]
+    lib.diffattn_bwd_v1.restype = i32
     lib.diffattn_decode_v1_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.diffattn_decode_v1_workspace_bytes.restype = sz
     lib.diffattn_decode_v1.argtypes = [T, T, T, T, T, T, i32, i32, i32, i32, i32, L, f32, u32, i32,
@@ -384,3 +400,80 @@ def diffattn_decode_paged(q1, q2, k_pages, v_pages, block_table, seq_lens, lq1=N
             max_blocks, int(max_len), dt, ctypes.byref(lam), int(num_splits), workspace.data_ptr(),
             ws_bytes, st), "diffattn_decode_paged")
     return out
+
+
+def diffattn_v1_train_stash_bytes(B, H, N, d) -> int:
+    return int(load_library().diffattn_v1_train_stash_bytes(B, H, N, d))
+
+
+def diffattn_bwd_v1_workspace_bytes(B, H, N, d) -> int:
+    return int(load_library().diffattn_bwd_v1_workspace_bytes(B, H, N, d))
+
+
+def diffattn_fwd_v1_train(q1, q2, k1, k2, v, lq1=None, lk1=None, lq2=None, lk2=None, layer=1, *,
+                          out=None, causal=True, eps=1e-5, stash=None, lambda_override=None,
+                          lambda_out=None, stream=None):
+    """V1 forward (bf16) that also fills the stash the backward pass reads; returns (out, stash).
+    ``stash`` is a GPU byte tensor of at least ``diffattn_v1_train_stash_bytes`` bytes."""
+    torch = _torch()
+    B, H, N, d = q1.shape
+    if out is None:
+        out = torch.empty((B, H, N, v.shape[-1]), dtype=q1.dtype, device=q1.device)
+    need = diffattn_v1_train_stash_bytes(B, H, N, d)
+    if stash is None:
+        stash = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    if not stash.is_cuda or not stash.is_contiguous():
+        raise ValueError("stash must be a contiguous GPU tensor")
+    dt = _dtype_code(q1)
+    descs = [_desc(q1, "q1", (B, H, N, d)), _desc(q2, "q2", (B, H, N, d)),
+             _desc(k1, "k1", (B, H, N, d)), _desc(k2, "k2", (B, H, N, d)),
+             _desc(v, "v", (B, H, N, 2 * d)), _desc(out, "out", (B, H, N, 2 * d))]
+    lam = _lambda(lq1, lk1, lq2, lk2, layer, H, lambda_override, lambda_out, q1.device)
+    with torch.cuda.device(q1.device):
+        st = _stream(q1.device, stream)
+        _check(load_library().diffattn_fwd_v1_train(
+            *descs, B, H, N, d, dt, ctypes.byref(lam), 1 if causal else 0, float(eps),
+            stash.data_ptr(), stash.numel() * stash.element_size(), st), "diffattn_fwd_v1_train")
+    return out, stash
+
+
+def diffattn_bwd_v1(q1, q2, k1, k2, v, dy, lq1=None, lk1=None, lq2=None, lk2=None, layer=1, *,
+                    stash, causal=True, eps=1e-5, workspace=None, grads=None,
+                    lambda_override=None, stream=None):
+    """Gradients of the V1 output for upstream gradient dy [B, H, N, 2d] (bf16).  Returns a dict
+    of fp32 GPU tensors: dq1, dq2, dk1, dk2 [B, H, N, d], dv [B, H, N, 2d] and (unless
+    ``lambda_override`` is given) dlq1, dlk1, dlq2, dlk2 [H, dl]."""
+    torch = _torch()
+    B, H, N, d = q1.shape
+    dev = q1.device
+    dl = lq1.shape[-1] if lq1 is not None else 1
+    if grads is None:
+        grads = {k: torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for k in ("dq1", "dq2", "dk1", "dk2")}
+        grads["dv"] = torch.empty((B, H, N, 2 * d), dtype=torch.float32, device=dev)
+        if lambda_override is None:
+            for k in ("dlq1", "dlk1", "dlq2", "dlk2"):
+                grads[k] = torch.empty((H, dl), dtype=torch.float32, device=dev)
+    for k, shape in (("dq1", (B, H, N, d)), ("dq2", (B, H, N, d)), ("dk1", (B, H, N, d)),
+                     ("dk2", (B, H, N, d)), ("dv", (B, H, N, 2 * d))):
+        x = grads[k]
+        if x.dtype != torch.float32 or tuple(x.shape) != shape or not x.is_contiguous() or not x.is_cuda:
+            raise ValueError(f"{k} must be a contiguous float32 GPU tensor of shape {shape}")
+    need = diffattn_bwd_v1_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    dt = _dtype_code(q1)
+    descs = [_desc(q1, "q1", (B, H, N, d)), _desc(q2, "q2", (B, H, N, d)),
+             _desc(k1, "k1", (B, H, N, d)), _desc(k2, "k2", (B, H, N, d)),
+             _desc(v, "v", (B, H, N, 2 * d)), _desc(dy, "dy", (B, H, N, 2 * d))]
+    lam = _lambda(lq1, lk1, lq2, lk2, layer, H, lambda_override, None, dev)
+    lg = DaLambdaGrad()
+    if lambda_override is None:
+        lg.dlq1, lg.dlk1, lg.dlq2, lg.dlk2 = (grads[k].data_ptr() for k in ("dlq1", "dlk1", "dlq2", "dlk2"))
+    with torch.cuda.device(dev):
+        st = _stream(dev, stream)
+        _check(load_library().diffattn_bwd_v1(
+            *descs, *(grads[k].data_ptr() for k in ("dq1", "dq2", "dk1", "dk2", "dv")),
+            B, H, N, d, dt, ctypes.byref(lam), ctypes.byref(lg), 1 if causal else 0, float(eps),
+            stash.data_ptr(), stash.numel() * stash.element_size(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), st), "diffattn_bwd_v1")
+    return grads

@@ -106,7 +106,7 @@ namespace {
 da_status fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2, da_tensor v,
                  da_tensor out, int32_t B, int32_t H, int32_t N, int32_t d, da_dtype dtype,
                  const da_lambda* lam, int32_t causal, int32_t window, float eps, uint32_t flags,
-                 void* stream) {
+                 void* stream, float* stash = nullptr) {
   if (B < 0 || H < 0 || N < 0 || window < 0) return DA_ERR_SHAPE;
   if (window > 0 && !causal) return DA_ERR_SHAPE;  // the window is a causal one
   if (B == 0 || H == 0 || N == 0) return DA_OK;
@@ -136,6 +136,11 @@ da_status fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2, da_tens
   p.eps = eps;
   p.out_scale = (float)(1.0 - diffattn_lambda_init(lam->layer));
   p.lam = lambda_args(lam);
+  if (stash != nullptr) {
+    const int64_t bhn = (int64_t)B * H * N;
+    p.stash_o = stash;                      // [2, B, H, N, 2d]
+    p.stash_lse = stash + 2 * bhn * 2 * d;  // rows 0 and 1 of [4, B, H, N]
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dtype == DA_F32) return hip_status(da::launch_v1_f32(p, st));
   for (const da_tensor* t : {&q1, &q2, &k1, &k2, &v})
@@ -255,6 +260,89 @@ da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tenso
   p.ws_ml = p.ws_acc + n_rows * D;
   p.lam = lambda_args(lam);
   return hip_status(da::launch_decode_v2(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t diffattn_v1_train_stash_bytes(int32_t B, int32_t H, int32_t N, int32_t d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d != 64) return 0;
+  const int64_t bhn = (int64_t)B * H * N;
+  return (size_t)((2 * bhn * 2 * d + 4 * bhn) * (int64_t)sizeof(float));
+}
+
+size_t diffattn_bwd_v1_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d != 64) return 0;
+  const int64_t bhn = (int64_t)B * H * N;
+  return (size_t)(bhn * 2 * d * 2 + bhn * (int64_t)sizeof(float));
+}
+
+da_status diffattn_fwd_v1_train(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2,
+                                da_tensor v, da_tensor out, int32_t B, int32_t H, int32_t N,
+                                int32_t d, da_dtype dtype, const da_lambda* lam, int32_t causal,
+                                float eps, void* stash, size_t stash_bytes, void* stream) {
+  if (B < 0 || H < 0 || N < 0) return DA_ERR_SHAPE;
+  if (B == 0 || H == 0 || N == 0) return DA_OK;
+  if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
+  if (d != 64) return d <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * N * 16 >= ((int64_t)1 << 32)) return DA_ERR_UNSUPPORTED;
+  const size_t need = diffattn_v1_train_stash_bytes(B, H, N, d);
+  if (stash == nullptr || !aligned16(stash) || stash_bytes < need) return DA_ERR_WORKSPACE;
+  return fwd_v1(q1, q2, k1, k2, v, out, B, H, N, d, dtype, lam, causal, 0, eps, 0u, stream,
+                static_cast<float*>(stash));
+}
+
+da_status diffattn_bwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2, da_tensor v,
+                          da_tensor dy, float* dq1, float* dq2, float* dk1, float* dk2, float* dv,
+                          int32_t B, int32_t H, int32_t N, int32_t d, da_dtype dtype,
+                          const da_lambda* lam, const da_lambda_grad* dlam, int32_t causal,
+                          float eps, const void* stash, size_t stash_bytes, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || N < 0) return DA_ERR_SHAPE;
+  if (B == 0 || H == 0 || N == 0) return DA_OK;
+  if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
+  if (d != 64) return d <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return DA_ERR_SHAPE;
+  if ((int64_t)B * H > (int64_t)INT32_MAX || (N + 63) / 64 > kMaxGridY || (N + 3) / 4 > INT32_MAX)
+    return DA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * N * 16 >= ((int64_t)1 << 32)) return DA_ERR_UNSUPPORTED;
+  for (const da_tensor* t : {&q1, &q2, &k1, &k2, &v, &dy}) {
+    const da_status s = check_tensor(*t, 2);
+    if (s != DA_OK) return s;
+    if (t != &dy && !rows_fit_32bit(*t, N, 2)) return DA_ERR_UNSUPPORTED;
+  }
+  for (const float* g : {dq1, dq2, dk1, dk2, dv})
+    if (g == nullptr || !aligned16(g)) return DA_ERR_NULL;
+  da_status s = check_lambda(lam, 256);
+  if (s != DA_OK) return s;
+  if (lam->lambda_override == nullptr &&
+      (dlam == nullptr || !dlam->dlq1 || !dlam->dlk1 || !dlam->dlq2 || !dlam->dlk2))
+    return DA_ERR_NULL;
+  if (stash == nullptr || !aligned16(stash) || stash_bytes < diffattn_v1_train_stash_bytes(B, H, N, d))
+    return DA_ERR_WORKSPACE;
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < diffattn_bwd_v1_workspace_bytes(B, H, N, d))
+    return DA_ERR_WORKSPACE;
+
+  da::BwdParams p{};
+  p.q1 = q1.ptr; p.q2 = q2.ptr; p.k1 = k1.ptr; p.k2 = k2.ptr; p.v = v.ptr; p.dy = dy.ptr;
+  p.sq1 = strides(q1); p.sq2 = strides(q2); p.sk1 = strides(k1); p.sk2 = strides(k2);
+  p.sv = strides(v); p.sdy = strides(dy);
+  p.dq1 = dq1; p.dq2 = dq2; p.dk1 = dk1; p.dk2 = dk2; p.dv = dv;
+  p.B = B; p.H = H; p.N = N;
+  p.causal = causal ? 1 : 0;
+  p.scale = (float)(1.0 / std::sqrt((double)d));
+  p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  p.eps = eps;
+  p.g = (float)(1.0 - diffattn_lambda_init(lam->layer));
+  const int64_t bhn = (int64_t)B * H * N;
+  float* st = static_cast<float*>(const_cast<void*>(stash));
+  p.stash_o = st;
+  p.lse_d = st + 2 * bhn * 2 * d;
+  p.d_o = workspace;
+  p.dl_row = reinterpret_cast<float*>(static_cast<char*>(workspace) + bhn * 2 * d * 2);
+  p.lam = lambda_args(lam);
+  if (dlam != nullptr) {
+    p.dlq1 = dlam->dlq1; p.dlk1 = dlam->dlk1; p.dlq2 = dlam->dlq2; p.dlk2 = dlam->dlk2;
+  }
+  return hip_status(da::launch_bwd_v1(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 da_status diffattn_decode_paged(da_tensor q1, da_tensor q2, const void* k_pages,

@@ -1,0 +1,509 @@
+// Backward pass of the V1 differential attention for gfx950: bf16 inputs, fp32 accumulation,
+// fp32 gradients.
+//
+// What is differentiated (Ultralytics glossary "Differential Transformer", section "Cómo funciona
+// la atención diferencial"; ai-engineering.academy "Atención Diferencial (V2)", section "La idea
+// diferencial"): per head, S_b = Q_b K_b^T / sqrt(d), A_b = softmax(S_b), O = A_1 V - lambda A_2 V,
+// y = (1 - lambda_init) O / sqrt(mean(O^2) + eps), lambda = exp(<lq1,lk1>) - exp(<lq2,lk2>) +
+// lambda_init.  The chain rule gives
+//   dO   = g r dy - g r^3 (O . dy) O / 2d          (g = 1 - lambda_init, r = 1/rms(O))
+//   dV   = A_1^T dO - lambda A_2^T dO
+//   dS_b = A_b * (dP_b - D_b),  dP_1 = dO V^T, dP_2 = -lambda dO V^T,
+//   D_1  = dO . O_1,  D_2 = -lambda dO . O_2       (row-wise; O_b = A_b V from the forward)
+//   dQ_b = dS_b K_b / sqrt(d),  dK_b = dS_b^T Q_b / sqrt(d),
+//   dlambda = -sum(dO . O_2), and the four lambda vectors through the exponentials.
+//
+// Kernels (A_b is never stored: each kernel rebuilds the weights it needs from the scores and the
+// forward's base-2 log-sum-exp, P = exp2(s log2(e)/sqrt(d) - LSE)):
+//  * bwd_prep: one wavefront per row: O, r, dO (stored bf16 for the MFMAs), D_1, D_2 and the
+//    row's share of dlambda.
+//  * bwd_dkdv: one 256-thread workgroup per 64 keys of a head; its waves are (branch, 32-key
+//    half).  Each wave keeps its keys' K and V as MFMA operands in registers and streams 32-row
+//    query tiles (Q_1, Q_2, dO, LSE, D) through LDS: S = Q K^T, P, dO V^T, dS on 32x32x16 bf16
+//    MFMAs with the accumulator layout feeding the next product directly (as in the forward);
+//    dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read by ds_read_b64_tr_b16.
+//    The two branch waves of a key half add their dV parts through LDS at the end.
+//  * bwd_dq: one workgroup per 64 query rows, waves (branch, 32-row half) as in the forward,
+//    streaming K_1, K_2, V tiles: S^T = K Q^T, P^T, V dO^T, dS^T, dQ^T += K^T dS^T.
+//  * bwd_lambda: per head, the sum of the rows' dlambda shares and the four vector gradients.
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "tile_common.hpp"
+
+namespace da {
+namespace {
+
+using namespace tile;
+constexpr int kD = 64;        // query / key half width
+constexpr int kT = 32;        // rows (keys or queries) per tile
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float lam_of(const BwdParams& p, int h, int lane) {
+  return head_lambda(p.lam, h, lane);
+}
+
+// ---------------------------------------------------------------------------------------------
+// prep: dO through the norm, D_b, dlambda shares
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int bh = blockIdx.y;
+  const int b = bh / p.H, h = bh % p.H;
+  const float lam = lam_of(p, h, lane);
+  if (row >= p.N) return;  // wave-uniform; no barrier follows
+  const int64_t BHN = (int64_t)p.B * p.H * p.N;
+  const int64_t r = (int64_t)bh * p.N + row;
+  const float* o1 = p.stash_o + r * kDV;
+  const float* o2 = p.stash_o + (BHN + r) * kDV;
+  const bf16* dy = static_cast<const bf16*>(p.dy) + b * p.sdy.sb + h * p.sdy.sh + (int64_t)row * p.sdy.sn;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 a1 = *reinterpret_cast<const f32x2*>(o1 + 2 * lane);
+  const f32x2 a2 = *reinterpret_cast<const f32x2*>(o2 + 2 * lane);
+  const uint32_t yw = *reinterpret_cast<const uint32_t*>(dy + 2 * lane);
+  const float y0 = bf16_lo(yw), y1 = bf16_hi(yw);
+  const float x0 = a1[0] - lam * a2[0], x1 = a1[1] - lam * a2[1];
+  const float ss = wave_sum(x0 * x0 + x1 * x1);
+  const float dot = wave_sum(x0 * y0 + x1 * y1);
+  const float rr = rsqrtf(ss * (1.f / kDV) + p.eps);
+  const float k1 = p.g * rr, k2 = p.g * rr * rr * rr * dot * (1.f / kDV);
+  const float d0 = k1 * y0 - k2 * x0, d1 = k1 * y1 - k2 * x1;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 dq = {(bf16)d0, (bf16)d1};
+  *reinterpret_cast<bf16x2*>(static_cast<bf16*>(p.d_o) + r * kDV + 2 * lane) = dq;
+  // D_b from the rounded dO the MFMAs use, so that D_b equals the row sum of P_b * dP_b that
+  // they form (the softmax Jacobian's subtraction then cancels what it should)
+  const float r0 = (float)dq[0], r1 = (float)dq[1];
+  const float e1 = wave_sum(r0 * a1[0] + r1 * a1[1]);
+  const float e2 = wave_sum(r0 * a2[0] + r1 * a2[1]);
+  const float g2 = wave_sum(d0 * a2[0] + d1 * a2[1]);
+  if (lane == 0) {
+    p.lse_d[2 * BHN + r] = e1;           // D_1
+    p.lse_d[3 * BHN + r] = -lam * e2;    // D_2
+    p.dl_row[r] = -g2;                   // this row's share of dlambda (unrounded dO)
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK_1, dK_2, dV: per 64 keys of a head
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
+  // per stage: Q_1, Q_2 [32][64] (K layout), dO [32][128] (V layout), LSE_1, LSE_2, D_1, D_2 [32]
+  constexpr int QT = kT * kD;              // elements of one Q tile
+  constexpr int OT = kT * kDV;             // elements of the dO tile
+  // + 1 KB for the row data: one wavefront DMA writes 64 x 16 bytes, of which the first 512 hold
+  // LSE_1, LSE_2, D_1, D_2 (the rest read past the buffer's end and land as zeros)
+  constexpr int STAGE = 2 * QT + OT + 512;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
+  static_assert(2 * STAGE * 2 >= 2 * 64 * 64 * 4, "dV exchange must fit the tile buffers");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int br = w >> 1, kh = w & 1;
+  const int c = lane & 31, hh = lane >> 5;
+  const int bh = blockIdx.x;
+  const int b = bh / p.H, h = bh % p.H;
+  const int kb = (int)blockIdx.y;                 // heaviest (earliest keys) first
+  const int key0 = kb * 64;
+  const int kw = key0 + 32 * kh;                  // this wave's first key
+  const int N = p.N;
+  const float lam = lam_of(p, h, lane);
+  const float sl2 = p.scale_log2;
+  const int64_t BHN = (int64_t)p.B * p.H * N;
+
+  // this wave's K_b^T and V^T as B operands: lane n = key kw + c, k = 16 t + 8 hh .. + 7
+  bf16x8 kf[kD / 16];
+  bf16x8 vf[kDV / 16];
+  {
+    const bf16* kbase = static_cast<const bf16*>(br == 0 ? p.k1 : p.k2) +
+                        b * (br == 0 ? p.sk1.sb : p.sk2.sb) + h * (br == 0 ? p.sk1.sh : p.sk2.sh);
+    const int64_t ksn = br == 0 ? p.sk1.sn : p.sk2.sn;
+    const bf16* vbase = static_cast<const bf16*>(p.v) + b * p.sv.sb + h * p.sv.sh;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (uint32_t)(N * ksn * 2));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (uint32_t)(N * p.sv.sn * 2));
+#pragma unroll
+    for (int t = 0; t < kD / 16; ++t)
+      kf[t] = __builtin_bit_cast(bf16x8, bload16(rk, (uint32_t)((kw + c) * ksn * 2) + 32 * t + 16 * hh));
+#pragma unroll
+    for (int t = 0; t < kDV / 16; ++t)
+      vf[t] = __builtin_bit_cast(bf16x8, bload16(rv, (uint32_t)((kw + c) * p.sv.sn * 2) + 32 * t + 16 * hh));
+    __builtin_amdgcn_s_waitcnt(0);  // settle before the asm tile DMA starts
+  }
+
+  // ---- query tiles: DMA of Q_1 / Q_2 (1 KB each per wave), dO (2 KB per wave), row data
+  const uint32_t q1_row = (uint32_t)(p.sq1.sn * 2), q2_row = (uint32_t)(p.sq2.sn * 2);
+  const char* q1_base = static_cast<const char*>(p.q1) + 2 * (b * p.sq1.sb + h * p.sq1.sh);
+  const char* q2_base = static_cast<const char*>(p.q2) + 2 * (b * p.sq2.sb + h * p.sq2.sh);
+  const char* do_base = static_cast<const char*>(p.d_o) + (int64_t)bh * N * kDV * 2;
+  int q_lrow;
+  uint32_t q_lchunk, o_lane[2];
+  {
+    const int e = 512 * w + 8 * lane;      // element of a Q tile this lane's 16 bytes land on
+    q_lrow = e / kD;
+    q_lchunk = (uint32_t)((((e % kD) >> 3) ^ k_swz<kD>(q_lrow)) * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ev = 512 * (w + 4 * i) + 8 * lane;
+      const int vrow = ev >> 7;
+      const int slot = (ev & 127) >> 3;
+      const int lcol = ((((slot >> 1) ^ (2 * (vrow & 3)))) << 4) + ((slot & 1) << 3);
+      o_lane[i] = (uint32_t)vrow * (kDV * 2) + lcol * 2;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t r_ld = make_rsrc(p.lse_d, (uint32_t)(4 * BHN * 4));
+  auto issue_tile = [&](int q0, int buf) {
+    bf16* st = smem + buf * STAGE;
+    const int rows_left = N - q0;
+    const __amdgpu_buffer_rsrc_t r1 = make_rsrc(q1_base + (size_t)q0 * q1_row, (uint32_t)rows_left * q1_row);
+    const __amdgpu_buffer_rsrc_t r2 = make_rsrc(q2_base + (size_t)q0 * q2_row, (uint32_t)rows_left * q2_row);
+    dma16(r1, st + 512 * w, (uint32_t)q_lrow * q1_row + q_lchunk);
+    dma16(r2, st + QT + 512 * w, (uint32_t)q_lrow * q2_row + q_lchunk);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(do_base + (size_t)q0 * kDV * 2, (uint32_t)rows_left * kDV * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(ro, st + 2 * QT + 512 * (w + 4 * i), o_lane[i]);
+    if (w == 0) {
+      // lanes 0..31: 16 bytes of LSE_1, LSE_2, D_1, D_2 for rows q0 .. q0+31; the rest read past
+      // the buffer's end and land as zeros
+      const int k = lane >> 3, piece = lane & 7;
+      const uint32_t off = lane < 32 ? (uint32_t)((((int64_t)k * BHN + (int64_t)bh * N + q0) * 4) + piece * 16)
+                                     : (uint32_t)(4 * BHN * 4);
+      dma16(r_ld, st + 2 * QT + OT, off);
+    }
+  };
+
+  // ---- accumulators: dV^T [128 ch x 32 keys] (4 x 32x32), dK^T [64 d x 32 keys] (2 x 32x32)
+  f32x16 dv[4], dk[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[i][r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[i][r] = 0.f;
+
+  // LDS read offsets (elements within a stage)
+  //  A operand of S = Q K^T: Q row c, chunk 2t + hh
+  const int q_rd = (br == 0 ? 0 : QT) + k_off<kD>(c, 8 * hh);  // chunk t: XOR 32 bytes * t
+  //  A operand of dO V^T: dO row c, 16-byte chunk 2t + hh (V layout)
+  //  transposed reads (dO^T, Q^T): lane j of a 16-lane group addresses row 4 hh + j / 4 (+ 16 u,
+  //  + 8 upper), columns 32 blk + 16 dh + 4 (j % 4)
+  const int jj = lane & 15, dh = (lane >> 4) & 1;
+  const int trow = 4 * hh + (jj >> 2);
+  const int tcol = dh * 16 + 4 * (jj & 3);
+
+  const int nq = (N + kT - 1) / kT;
+  const int qt_begin = p.causal ? key0 / kT : 0;    // first query tile the workgroup needs
+  const int qt_wave = p.causal ? kw / kT : 0;       // first query tile with a row >= kw
+  const bool wave_has_keys = kw < N;
+
+  auto compute = [&](int qt, int buf) {
+    const bf16* st = smem + buf * STAGE;
+    const int q0 = qt * kT;
+    const float* rowd = reinterpret_cast<const float*>(st + 2 * QT + OT);  // [4][32]
+    // S[q][key]
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kD / 16; ++t) {
+      const int off = q_rd ^ (16 * t);  // elements: chunk 2t + hh, swizzle XOR on the chunk bits
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(st + off), kf[t], s, 0, 0, 0);
+    }
+    // X[q][key] = dO V^T
+    f32x16 x;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kDV / 16; ++t) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + 2 * QT + v_off(c, 16 * t + 8 * hh));
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[t], x, 0, 0, 0);
+    }
+    // P, dS (registers r: query q0 + 8 (r/4) + 4 hh + r % 4, key kw + c)
+    const int key = kw + c;
+    const float dscale = br == 0 ? 1.f : -lam;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ql = 8 * j + 4 * hh;
+      const f32x4 lse = *reinterpret_cast<const f32x4*>(rowd + br * kT + ql);
+      const f32x4 dd = *reinterpret_cast<const f32x4*>(rowd + (2 + br) * kT + ql);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * j + i;
+        const int q = q0 + ql + i;
+        const bool vis = q < N && key < N && (!p.causal || key <= q);
+        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse[i])) : 0.f;
+        const float dp = dscale * x[r];
+        s[r] = pr * dscale;                 // P' = P (branch 1) or -lambda P (branch 2), for dV
+        x[r] = pr * (dp - dd[i]);           // dS
+      }
+    }
+    // dV^T += dO^T P', dK^T += Q^T dS (B operands: 16-row halves of the accumulators)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float dummy = 0.f;
+      const bf16x8 pb = cvt8_sum(s, 8 * u, dummy);
+      const bf16x8 sb = cvt8_sum(x, 8 * u, dummy);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16* base = st + 2 * QT;
+        const u32x2 lo = lds_read_tr(base + v_off(16 * u + trow, 32 * db + tcol));
+        const u32x2 hi = lds_read_tr(base + v_off(16 * u + 8 + trow, 32 * db + tcol));
+        const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pb, dv[db], 0, 0, 0);
+      }
+#pragma unroll
+      for (int dbk = 0; dbk < 2; ++dbk) {
+        const bf16* base = st + (br == 0 ? 0 : QT);
+        const u32x2 lo = lds_read_tr(base + k_off<kD>(16 * u + trow, 32 * dbk + tcol));
+        const u32x2 hi = lds_read_tr(base + k_off<kD>(16 * u + 8 + trow, 32 * dbk + tcol));
+        const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
+        dk[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), sb, dk[dbk], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- main loop over query tiles (tile t+1 loads during tile t)
+  issue_tile(qt_begin * kT, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int qt = qt_begin; qt < nq; ++qt) {
+    const int buf = (qt - qt_begin) & 1;
+    if (qt + 1 < nq) issue_tile((qt + 1) * kT, buf ^ 1);
+    if (wave_has_keys && qt >= qt_wave) compute(qt, buf);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  // ---- epilogue: branch-2 waves hand their dV part to the branch-1 waves; write dK_b, dV
+  float* xb = reinterpret_cast<float*>(smem) + kh * (64 * 64);
+  if (br == 1) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xb[(db * 16 + r) * 64 + lane] = dv[db][r];
+  }
+  const int key = kw + c;
+  if (wave_has_keys && key < N) {
+    float* dkp = (br == 0 ? p.dk1 : p.dk2) + ((int64_t)bh * N + key) * kD;
+#pragma unroll
+    for (int dbk = 0; dbk < 2; ++dbk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v4 = {dk[dbk][4 * j] * p.scale, dk[dbk][4 * j + 1] * p.scale,
+                          dk[dbk][4 * j + 2] * p.scale, dk[dbk][4 * j + 3] * p.scale};
+        *reinterpret_cast<f32x4*>(dkp + dbk * 32 + 8 * j + 4 * hh) = v4;
+      }
+  }
+  __syncthreads();
+  if (br == 1 || !wave_has_keys || key >= N) return;
+  float* dvp = p.dv + ((int64_t)bh * N + key) * kDV;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 v4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v4[i] = dv[db][4 * j + i] + xb[(db * 16 + 4 * j + i) * 64 + lane];
+      *reinterpret_cast<f32x4*>(dvp + db * 32 + 8 * j + 4 * hh) = v4;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dQ_1, dQ_2: per 64 query rows
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
+  constexpr int KT = kT * kD;                  // one K tile
+  constexpr int STAGE = 2 * KT + kT * kDV;     // K_1 | K_2 | V
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int br = w >> 1, rh = w & 1;
+  const int c = lane & 31, hh = lane >> 5;
+  const int bh = blockIdx.x;
+  const int b = bh / p.H, h = bh % p.H;
+  const int rb = p.n_row_blocks - 1 - (int)blockIdx.y;   // heaviest first
+  const int row0 = rb * 64;
+  const int wrow = row0 + 32 * rh;
+  const int N = p.N;
+  const float lam = lam_of(p, h, lane);
+  const float sl2 = p.scale_log2;
+  const int64_t BHN = (int64_t)p.B * p.H * N;
+  const bool wave_has_rows = wrow < N;
+  const int qrow = wrow + c;
+
+  // Q_b^T and dO^T as B operands: lane n = query wrow + c, k = 16 t + 8 hh .. + 7
+  bf16x8 qf[kD / 16], of[kDV / 16];
+  float lse = 0.f, dd = 0.f;
+  {
+    const bf16* qb = static_cast<const bf16*>(br == 0 ? p.q1 : p.q2) +
+                     b * (br == 0 ? p.sq1.sb : p.sq2.sb) + h * (br == 0 ? p.sq1.sh : p.sq2.sh);
+    const int64_t qsn = br == 0 ? p.sq1.sn : p.sq2.sn;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (uint32_t)(N * qsn * 2));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<const char*>(p.d_o) + (int64_t)bh * N * kDV * 2,
+                                                (uint32_t)(N * kDV * 2));
+#pragma unroll
+    for (int t = 0; t < kD / 16; ++t)
+      qf[t] = __builtin_bit_cast(bf16x8, bload16(rq, (uint32_t)(qrow * qsn * 2) + 32 * t + 16 * hh));
+#pragma unroll
+    for (int t = 0; t < kDV / 16; ++t)
+      of[t] = __builtin_bit_cast(bf16x8, bload16(ro, (uint32_t)(qrow * kDV * 2) + 32 * t + 16 * hh));
+    if (qrow < N) {
+      lse = p.lse_d[(int64_t)br * BHN + (int64_t)bh * N + qrow];
+      dd = p.lse_d[(int64_t)(2 + br) * BHN + (int64_t)bh * N + qrow];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  // ---- key tiles: K_1, K_2 (1 KB DMA each per wave), V (2 KB per wave)
+  const uint32_t k1_row = (uint32_t)(p.sk1.sn * 2), k2_row = (uint32_t)(p.sk2.sn * 2);
+  const uint32_t v_row = (uint32_t)(p.sv.sn * 2);
+  const char* k1_base = static_cast<const char*>(p.k1) + 2 * (b * p.sk1.sb + h * p.sk1.sh);
+  const char* k2_base = static_cast<const char*>(p.k2) + 2 * (b * p.sk2.sb + h * p.sk2.sh);
+  const char* v_base = static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + h * p.sv.sh);
+  int k_lrow;
+  uint32_t k_lchunk, v_lane[2];
+  {
+    const int e = 512 * w + 8 * lane;
+    k_lrow = e / kD;
+    k_lchunk = (uint32_t)((((e % kD) >> 3) ^ k_swz<kD>(k_lrow)) * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ev = 512 * (w + 4 * i) + 8 * lane;
+      const int vrow = ev >> 7;
+      const int slot = (ev & 127) >> 3;
+      const int lcol = ((((slot >> 1) ^ (2 * (vrow & 3)))) << 4) + ((slot & 1) << 3);
+      v_lane[i] = (uint32_t)vrow * v_row + lcol * 2;
+    }
+  }
+  auto issue_tile = [&](int k0, int buf) {
+    bf16* st = smem + buf * STAGE;
+    const int rows_left = N - k0;
+    const __amdgpu_buffer_rsrc_t r1 = make_rsrc(k1_base + (size_t)k0 * k1_row, (uint32_t)rows_left * k1_row);
+    const __amdgpu_buffer_rsrc_t r2 = make_rsrc(k2_base + (size_t)k0 * k2_row, (uint32_t)rows_left * k2_row);
+    dma16(r1, st + 512 * w, (uint32_t)k_lrow * k1_row + k_lchunk);
+    dma16(r2, st + KT + 512 * w, (uint32_t)k_lrow * k2_row + k_lchunk);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v_base + (size_t)k0 * v_row, (uint32_t)rows_left * v_row);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(rv, st + 2 * KT + 512 * (w + 4 * i), v_lane[i]);
+  };
+
+  f32x16 dq[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
+
+  const int k_rd = (br == 0 ? 0 : KT) + k_off<kD>(c, 8 * hh);
+  const int jj = lane & 15, dh = (lane >> 4) & 1;
+  const int trow = 4 * hh + (jj >> 2);
+  const int tcol = dh * 16 + 4 * (jj & 3);
+  const float dscale = br == 0 ? 1.f : -lam;
+
+  auto compute = [&](int kt, int buf) {
+    const bf16* st = smem + buf * STAGE;
+    const int k0 = kt * kT;
+    f32x16 s, x;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; x[r] = 0.f; }
+#pragma unroll
+    for (int t = 0; t < kD / 16; ++t)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(st + (k_rd ^ (16 * t))), qf[t], s, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < kDV / 16; ++t) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + 2 * KT + v_off(c, 16 * t + 8 * hh));
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, of[t], x, 0, 0, 0);
+    }
+    // registers r: key k0 + 8 (r/4) + 4 hh + r % 4; query qrow
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const bool vis = key < N && qrow < N && (!p.causal || key <= qrow);
+      const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse)) : 0.f;
+      s[r] = pr * (dscale * x[r] - dd);     // dS^T
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float dummy = 0.f;
+      const bf16x8 sb = cvt8_sum(s, 8 * u, dummy);
+#pragma unroll
+      for (int dbk = 0; dbk < 2; ++dbk) {
+        const bf16* base = st + (br == 0 ? 0 : KT);
+        const u32x2 lo = lds_read_tr(base + k_off<kD>(16 * u + trow, 32 * dbk + tcol));
+        const u32x2 hi = lds_read_tr(base + k_off<kD>(16 * u + 8 + trow, 32 * dbk + tcol));
+        const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
+        dq[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), sb, dq[dbk], 0, 0, 0);
+      }
+    }
+  };
+
+  const int kv_end = p.causal ? min(N, row0 + 64) : N;
+  const int ntiles = (kv_end + kT - 1) / kT;
+  const int last_key = p.causal ? min(N, wrow + 32) : N;
+  const int nt_wave = wave_has_rows ? min(ntiles, (last_key + kT - 1) / kT) : 0;
+  issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    if (kt + 1 < ntiles) issue_tile((kt + 1) * kT, (kt + 1) & 1);
+    if (kt < nt_wave) compute(kt, kt & 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (!wave_has_rows || qrow >= N) return;
+  float* dqp = (br == 0 ? p.dq1 : p.dq2) + ((int64_t)bh * N + qrow) * kD;
+#pragma unroll
+  for (int dbk = 0; dbk < 2; ++dbk)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v4 = {dq[dbk][4 * j] * p.scale, dq[dbk][4 * j + 1] * p.scale,
+                        dq[dbk][4 * j + 2] * p.scale, dq[dbk][4 * j + 3] * p.scale};
+      *reinterpret_cast<f32x4*>(dqp + dbk * 32 + 8 * j + 4 * hh) = v4;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dlambda per head and the four vector gradients (one wavefront per head)
+__global__ __launch_bounds__(64) void bwd_lambda_kernel(const BwdParams p) {
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x;
+  float s = 0.f;
+  for (int b = 0; b < p.B; ++b) {
+    const float* dl = p.dl_row + ((int64_t)b * p.H + h) * p.N;
+    for (int i = lane; i < p.N; i += 64) s += dl[i];
+  }
+  const float dlam = wave_sum(s);
+  const LambdaArgs& L = p.lam;
+  if (L.override_ != nullptr) return;  // lambda given directly: no vector gradients
+  const int64_t base = (int64_t)h * L.dl;
+  float a = 0.f, c2 = 0.f;
+  for (int e = lane; e < L.dl; e += 64) {
+    a = fmaf(L.lq1[base + e], L.lk1[base + e], a);
+    c2 = fmaf(L.lq2[base + e], L.lk2[base + e], c2);
+  }
+  const float ea = expf(wave_sum(a)), eb = expf(wave_sum(c2));
+  for (int e = lane; e < L.dl; e += 64) {
+    p.dlq1[base + e] = dlam * ea * L.lk1[base + e];
+    p.dlk1[base + e] = dlam * ea * L.lq1[base + e];
+    p.dlq2[base + e] = -dlam * eb * L.lk2[base + e];
+    p.dlk2[base + e] = -dlam * eb * L.lq2[base + e];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_v1(const BwdParams& p, hipStream_t stream) {
+  BwdParams q = p;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((p.N + 3) / 4, p.B * p.H), dim3(kThreads), 0, stream, q);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  q.n_row_blocks = (p.N + 63) / 64;
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.B * p.H, q.n_row_blocks), dim3(kThreads), 0, stream, q);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.B * p.H, q.n_row_blocks), dim3(kThreads), 0, stream, q);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_lambda_kernel, dim3(p.H), dim3(64), 0, stream, q);
+  return hipGetLastError();
+}
+
+}  // namespace da

@@ -43,6 +43,42 @@ struct PrefillParams {
   float eps;
   float out_scale;       // 1 - lambda_init
   LambdaArgs lam;
+  // V1 training forward: per-branch normalised outputs O_b = A_b V and base-2 log-sum-exp of the
+  // scaled scores, for the backward pass (null: not written)
+  float* stash_o;        // [2, B, H, N, 2d]
+  float* stash_lse;      // [2, B, H, N]
+};
+
+// V1 backward.  Inputs bf16 (strided); gradients fp32, contiguous.
+struct BwdParams {
+  const void* q1;
+  const void* q2;
+  const void* k1;
+  const void* k2;
+  const void* v;
+  const void* dy;
+  Strides sq1, sq2, sk1, sk2, sv, sdy;
+  float* dq1;            // [B, H, N, d]
+  float* dq2;
+  float* dk1;
+  float* dk2;
+  float* dv;             // [B, H, N, 2d]
+  int32_t B, H, N;
+  int32_t causal;
+  int32_t n_row_blocks;  // 64-row query blocks (dQ) / 64-key blocks (dK, dV)
+  float scale;           // 1 / sqrt(d)
+  float scale_log2;      // log2(e) / sqrt(d)
+  float eps;
+  float g;               // 1 - lambda_init
+  const float* stash_o;  // [2, B, H, N, 2d] from the training forward
+  float* lse_d;          // [4, B, H, N]: LSE_1, LSE_2 (forward, base 2), D_1, D_2 (prep)
+  void* d_o;             // [B, H, N, 2d] bf16: upstream gradient through the norm (prep)
+  float* dl_row;         // [B, H, N]: each row's share of dlambda (prep)
+  LambdaArgs lam;
+  float* dlq1;           // [H, dl] lambda-vector gradients
+  float* dlk1;
+  float* dlq2;
+  float* dlk2;
 };
 
 // One V2 decode step: split-K partial pass + combine pass.

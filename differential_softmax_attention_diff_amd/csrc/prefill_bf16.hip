@@ -44,101 +44,16 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "tile_common.hpp"
 
 namespace da {
 namespace {
 
-constexpr int kDV = 128;    // value width
+using namespace tile;
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for the running max
 constexpr float kCapSum = 4096.f;    // largest lane weight sum per tile (2^12) before the max moves
 constexpr float kF16Max = 65504.f;   // largest fp16 magnitude
-constexpr int kRsrcWord3 = 0x00020000;  // buffer resource flags word for gfx9-family targets
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-
-// XOR swizzle of 16-byte chunk indices in a dense K tile row (64 banks of 4 bytes).
-template <int DQK>
-__device__ __forceinline__ int k_swz(int row) {
-  return DQK == 64 ? ((row >> 1) & 7) : (row & 15);
-}
-// Element offset of (row, col) in a dense K tile.
-template <int DQK>
-__device__ __forceinline__ int k_off(int row, int col) {
-  return row * DQK + ((((col >> 3) ^ k_swz<DQK>(row))) << 3) + (col & 7);
-}
-// Element offset of (row, col) in a dense V tile (128 channels) with 32-byte chunks swizzled.
-__device__ __forceinline__ int v_off(int row, int col) {
-  return row * kDV + ((((col >> 4) ^ (2 * (row & 3)))) << 4) + (col & 15);
-}
-
-// sum of x over the lane pair (l, l ^ 32).  (A v_permlane32_swap formulation was tried: the
-// compiler treated both of its results as one value, so lane exchanges go through ds_bpermute.)
-__device__ __forceinline__ float pair_sum(float x) { return x + __shfl_xor(x, 32); }
-
-// Round 8 consecutive weights of s to a packed MFMA operand and add the rounded values to l
-// (v_dot2 of each packed pair against (1, 1)).  Each pair is converted and summed on its own.
-__device__ __forceinline__ bf16x8 cvt8_sum(const f32x16& s, int base, float& l) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
-  u32x4 w;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x2 h = {(bf16)s[base + 2 * i], (bf16)s[base + 2 * i + 1]};
-    l = __builtin_amdgcn_fdot2_f32_bf16(h, one, l, false);
-    w[i] = __builtin_bit_cast(uint32_t, h);
-  }
-  return __builtin_bit_cast(bf16x8, w);
-}
-__device__ __forceinline__ f16x8 cvt8h_sum(const f32x16& s, int base, float& l) {
-  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
-  u32x4 w;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 h = {(_Float16)s[base + 2 * i], (_Float16)s[base + 2 * i + 1]};
-    l = __builtin_amdgcn_fdot2(h, one, l, false);
-    w[i] = __builtin_bit_cast(uint32_t, h);
-  }
-  return __builtin_bit_cast(f16x8, w);
-}
-
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  f16x2 h = {(_Float16)a, (_Float16)b};
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-// Transposing LDS read (see file header): returns 4 consecutive-row elements of one column.
-__device__ __forceinline__ u32x2 lds_read_tr(const bf16* p) {
-  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (__attribute__((address_space(3))) bf16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
-}
-
-// One wavefront-wide 16-byte-per-lane DMA from a buffer into LDS (lane i lands at lds + 16 i).
-// Issued from inline asm so that the compiler does not treat it as aliasing every later LDS read
-// (it would otherwise wait for all outstanding DMA before each one, defeating the prefetch); the
-// kernels order these writes themselves with explicit vmcnt waits and barriers.  M0 holds the LDS
-// base; one wait state separates the M0 write from the DMA.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, uint32_t voff) {
-  const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void*)lds;
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
-      :
-      : "s"(m0v), "v"(voff), "s"(r)
-      : "memory");
-}
-
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
-
 constexpr int kSBN = 32;  // keys per tile
 // Tile buffers in LDS.  Three (loads two tiles ahead) measured 7 % slower for V1: 48 KB per
 // workgroup allows 3 workgroups per CU instead of 4, and load latency was not the limit.
@@ -538,6 +453,24 @@ void prefill_kernel(const PrefillParams p) {
   // ---- epilogue: branch-2 waves publish lambda acc_2 / l_2; branch-1 waves finish the rows
   const float lam = head_lambda(p.lam, qh, lane);
   if (p.lam.out != nullptr && b == 0 && rb == 0 && w == 0 && lane == 0) p.lam.out[qh] = lam;
+  if constexpr (!V2) {
+    // training forward: this branch's normalised output and log-sum-exp (base 2) per row
+    if (p.stash_o != nullptr && wave_has_rows && wrow + c < N) {
+      const float l = pair_sum(lrun);
+      const float inv = 1.f / l;
+      const int64_t row = (((int64_t)br * p.B + b) * p.heads + qh) * N + wrow + c;
+      float* o = p.stash_o + row * kDV;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 x = {acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv, acc[db][4 * j + 2] * inv,
+                           acc[db][4 * j + 3] * inv};
+          *reinterpret_cast<f32x4*>(o + db * 32 + 8 * j + 4 * hh) = x;
+        }
+      if (hh == 0) p.stash_lse[row] = mrun * sl2 + __log2f(l);
+    }
+  }
   float* xb = reinterpret_cast<float*>(smem) + rh * (64 * 64);
   if (br == 1 && wave_has_rows) {
     const float i2 = lam / pair_sum(lrun);

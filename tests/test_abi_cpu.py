@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_header_symbols_exported(da):
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 16, names
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n

@@ -1,0 +1,141 @@
+"""GPU parity of the V1 backward pass against the float64 backward oracle (itself pinned by
+autograd and finite differences).
+
+Gradients have no fixed scale, so each (batch, head) slice of a gradient is divided by its oracle
+RMS before the bound is applied.  The bound comes from the arithmetic: the three gradient
+products take one operand each in bf16 (the upstream gradient through the norm, the
+probabilities, and the score gradient dS = P * (dP - D)), with unit roundoff u = 2^-9, and dS
+itself inherits the rounding of dO through dP.  Each gradient entry is a sum over up to N such
+products whose exact value cancels (every row of dS sums to zero), so its rounding error, relative
+to the slice RMS, is a few u on average with tails of about ten u: re-running the oracle's
+float64 chain with only those operands rounded to bf16 gives a normalised max error of 1.0-1.5e-2
+on these cases.  The bar is BWD_MAX_TOL on the largest normalised error and BWD_RMS_TOL on the
+RMS of the normalised error -- twice the rounding's own figures, and far below the O(1) error of a
+dropped term, a sign or a transposed operand.  The lambda-vector gradients, sums over every row
+of the layer, are compared relative to their largest oracle entry."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from oracle import compare
+from tests.helpers import dev, dev_lambda, f64, log
+
+pytestmark = pytest.mark.gpu
+
+BWD_MAX_TOL = 5e-2
+BWD_RMS_TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def da():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import differential_softmax_attention_diff_amd as mod
+
+    mod.load_library()
+    return mod
+
+
+def _slice_stats(got, ref):
+    """max and RMS of |got - ref| / rms(ref) per (batch, head) slice.  A slice whose exact
+    gradient is nearly zero is measured against 1e-3 of the whole tensor's RMS, or 1e-6,
+    whichever is larger."""
+    g = got.reshape(got.shape[0] * got.shape[1], -1)
+    r = ref.reshape(ref.shape[0] * ref.shape[1], -1)
+    rms_all = float(np.sqrt(np.mean(r * r)))
+    rms = np.maximum(np.sqrt(np.mean(r * r, axis=1, keepdims=True)), max(1e-3 * rms_all, 1e-6))
+    e = np.abs(g - r) / rms
+    return {"max_abs": float(e.max()), "rms": float(np.sqrt(np.mean(e * e))),
+            "finite": bool(np.isfinite(g).all())}
+
+
+def _ok(st):
+    return st["finite"] and st["max_abs"] <= BWD_MAX_TOL and st["rms"] <= BWD_RMS_TOL
+
+
+def _run(da, t, layer, causal, dy):
+    import torch
+
+    args = [dev(t[k]) for k in ("q1", "q2", "k1", "k2", "v")]
+    lv = dev_lambda(t["lambda"][layer])
+    out, stash = da.diffattn_fwd_v1_train(*args, *lv, layer=layer, causal=causal)
+    g = da.diffattn_bwd_v1(*args, dev(dy), *lv, layer=layer, stash=stash, causal=causal)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in g.items()}
+
+
+def _dy(shape, seed):
+    rng = np.random.default_rng(seed)
+    return wl.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("B,H,N,causal", [
+    (1, 1, 1, True), (1, 2, 37, True), (2, 2, 64, True), (1, 2, 100, True), (1, 1, 257, True),
+    (1, 2, 70, False),
+])
+def test_bwd_v1_against_oracle(da, B, H, N, causal):
+    log(f"bwd v1 B={B} H={H} N={N} causal={causal}")
+    layer = 6
+    t = wl.make_v1(B, H, N, 64, "bf16", seed=N + 5 * H, layers=(layer,))
+    dy = _dy((B, H, N, 128), seed=N)
+    out, g = _run(da, t, layer, causal, dy)
+    ref = oracle.diff_attn_v1_backward(*(f64(t[k]) for k in ("q1", "q2", "k1", "k2", "v")),
+                                       t["lambda"][layer], layer, f64(dy), causal, 1e-5)
+    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
+        if N == 1 and k != "dv":
+            # One visible key: each softmax is the constant 1, so dQ and dK vanish exactly; the
+            # kernel leaves only the fp32 difference of two summation orders of dO . O_b.
+            assert np.max(np.abs(ref[k])) == 0.0
+            log(f"  {k} max |got| {np.max(np.abs(g[k])):.3e}")
+            assert np.max(np.abs(g[k])) <= 1e-5, k
+            continue
+        st = _slice_stats(g[k], ref[k])
+        log(f"  {k} {st}")
+        assert _ok(st), (k, st)
+    slack = np.zeros(H)
+    if N == 1:
+        # One row per head: O = (1 - lambda) V, and the norm makes the output blind to the scale of
+        # O, so dL/dlambda = -sum_j dO_j O2_j cancels down to about eps / mean(O^2) of its terms.
+        # Its fp32 rounding is then measured against those terms: sum_j |dO_j| |V_j|, with
+        # dO = dV / (1 - lambda) (both softmaxes are the constant 1).
+        lam = oracle.lambda_value(*t["lambda"][layer], layer)
+        terms = np.sum(np.abs(ref["dv"][0, :, 0]) * np.abs(f64(t["v"])[0, :, 0]), axis=-1)
+        slack = 1e-5 * terms / np.abs(1.0 - lam)
+    for k in ("dlq1", "dlk1", "dlq2", "dlk2"):
+        # the vector gradients are dL/dlambda times a per-element chain factor
+        factor = np.abs(ref[k]) / np.maximum(np.abs(ref["dlam"]), 1e-300)[:, None]
+        bound = compare.BF16_MAX_ABS_TOL * np.max(np.abs(ref[k])) + slack[:, None] * factor
+        err = np.max(np.abs(g[k] - ref[k]) / bound)
+        log(f"  {k} err / bound {err:.3e}")
+        assert err <= 1.0, (k, err)
+
+
+def test_train_forward_output_equals_forward(da):
+    import torch
+
+    t = wl.make_v1(2, 3, 300, 64, "bf16", seed=3, layers=(12,))
+    args = [dev(t[k]) for k in ("q1", "q2", "k1", "k2", "v")]
+    lv = dev_lambda(t["lambda"][12])
+    a = da.diffattn_fwd_v1(*args, *lv, layer=12)
+    b, _ = da.diffattn_fwd_v1_train(*args, *lv, layer=12)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_bwd_v1_workload_slice(da):
+    """The 4K workload's shape for two heads (B=1, H=2, N=4096), all gradients."""
+    layer = 12
+    t = wl.make_v1(1, 2, 4096, 64, "bf16", seed=1002, layers=(layer,))
+    dy = _dy((1, 2, 4096, 128), seed=77)
+    log("bwd v1 N=4096 H=2")
+    _, g = _run(da, t, layer, True, dy)
+    ref = oracle.diff_attn_v1_backward(*(f64(t[k]) for k in ("q1", "q2", "k1", "k2", "v")),
+                                       t["lambda"][layer], layer, f64(dy), True, 1e-5)
+    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
+        st = _slice_stats(g[k], ref[k])
+        log(f"  {k} {st}")
+        assert _ok(st), (k, st)
