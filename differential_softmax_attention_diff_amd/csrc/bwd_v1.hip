@@ -15,8 +15,8 @@
 //
 // Kernels (A_b is never stored: each kernel rebuilds the weights it needs from the scores and the
 // forward's base-2 log-sum-exp, P = exp2(s log2(e)/sqrt(d) - LSE)):
-//  * bwd_prep: one wavefront per row: O, r, dO (stored bf16 for the MFMAs), D_1, D_2 and the
-//    row's share of dlambda.
+//  * bwd_prep: 16 lanes per row: O, r, dO (stored bf16 for the MFMAs), D_1, D_2 and the row's
+//    share of dlambda.
 //  * bwd_dkdv: one 256-thread workgroup per 64 keys of a head; its waves are (branch, 32-key
 //    half).  Each wave keeps its keys' K and V as MFMA operands in registers and streams 32-row
 //    query tiles (Q_1, Q_2, dO, LSE, D) through LDS: S = Q K^T, P, dO V^T, dS on 32x32x16 bf16
@@ -25,7 +25,10 @@
 //    The two branch waves of a key half add their dV parts through LDS at the end.
 //  * bwd_dq: one workgroup per 64 query rows, waves (branch, 32-row half) as in the forward,
 //    streaming K_1, K_2, V tiles: S^T = K Q^T, P^T, V dO^T, dS^T, dQ^T += K^T dS^T.
-//  * bwd_lambda: per head, the sum of the rows' dlambda shares and the four vector gradients.
+//  * bwd_lambda: per head, the sum of the rows' dlambda shares (one 1024-thread workgroup, fixed
+//    order) and the four vector gradients.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "tile_common.hpp"
@@ -44,42 +47,80 @@ __device__ __forceinline__ float lam_of(const BwdParams& p, int h, int lane) {
 
 // ---------------------------------------------------------------------------------------------
 // prep: dO through the norm, D_b, dlambda shares
+// 16 lanes per row (8 of its 2d channels each), four rows per wavefront pass, two passes
+constexpr int kPrepRowsPerWave = 8;
+constexpr int kPrepRowsPerBlock = kPrepRowsPerWave * (kThreads / 64);
+
+// sum over the 16 lanes that share a row (xor partners stay inside the group)
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int bh = blockIdx.y;
+  const int w = threadIdx.x >> 6;
+  const int sub = lane & 15;
+  const int bh = blockIdx.x;
   const int b = bh / p.H, h = bh % p.H;
   const float lam = lam_of(p, h, lane);
-  if (row >= p.N) return;  // wave-uniform; no barrier follows
   const int64_t BHN = (int64_t)p.B * p.H * p.N;
-  const int64_t r = (int64_t)bh * p.N + row;
-  const float* o1 = p.stash_o + r * kDV;
-  const float* o2 = p.stash_o + (BHN + r) * kDV;
-  const bf16* dy = static_cast<const bf16*>(p.dy) + b * p.sdy.sb + h * p.sdy.sh + (int64_t)row * p.sdy.sn;
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 a1 = *reinterpret_cast<const f32x2*>(o1 + 2 * lane);
-  const f32x2 a2 = *reinterpret_cast<const f32x2*>(o2 + 2 * lane);
-  const uint32_t yw = *reinterpret_cast<const uint32_t*>(dy + 2 * lane);
-  const float y0 = bf16_lo(yw), y1 = bf16_hi(yw);
-  const float x0 = a1[0] - lam * a2[0], x1 = a1[1] - lam * a2[1];
-  const float ss = wave_sum(x0 * x0 + x1 * x1);
-  const float dot = wave_sum(x0 * y0 + x1 * y1);
-  const float rr = rsqrtf(ss * (1.f / kDV) + p.eps);
-  const float k1 = p.g * rr, k2 = p.g * rr * rr * rr * dot * (1.f / kDV);
-  const float d0 = k1 * y0 - k2 * x0, d1 = k1 * y1 - k2 * x1;
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 dq = {(bf16)d0, (bf16)d1};
-  *reinterpret_cast<bf16x2*>(static_cast<bf16*>(p.d_o) + r * kDV + 2 * lane) = dq;
-  // D_b from the rounded dO the MFMAs use, so that D_b equals the row sum of P_b * dP_b that
-  // they form (the softmax Jacobian's subtraction then cancels what it should)
-  const float r0 = (float)dq[0], r1 = (float)dq[1];
-  const float e1 = wave_sum(r0 * a1[0] + r1 * a1[1]);
-  const float e2 = wave_sum(r0 * a2[0] + r1 * a2[1]);
-  const float g2 = wave_sum(d0 * a2[0] + d1 * a2[1]);
-  if (lane == 0) {
-    p.lse_d[2 * BHN + r] = e1;           // D_1
-    p.lse_d[3 * BHN + r] = -lam * e2;    // D_2
-    p.dl_row[r] = -g2;                   // this row's share of dlambda (unrounded dO)
+#pragma unroll
+  for (int it = 0; it < kPrepRowsPerWave / 4; ++it) {
+    const int row = blockIdx.y * kPrepRowsPerBlock + w * kPrepRowsPerWave + 4 * it + (lane >> 4);
+    // rows past N compute on row N-1 (so every lane of a group takes part) and store nothing
+    const int rc = min(row, p.N - 1);
+    const int64_t r = (int64_t)bh * p.N + rc;
+    const float* o1 = p.stash_o + r * kDV + 8 * sub;
+    const float* o2 = p.stash_o + (BHN + r) * kDV + 8 * sub;
+    const bf16* dy = static_cast<const bf16*>(p.dy) + b * p.sdy.sb + h * p.sdy.sh + (int64_t)rc * p.sdy.sn + 8 * sub;
+    const f32x4 a1l = *reinterpret_cast<const f32x4*>(o1), a1h = *reinterpret_cast<const f32x4*>(o1 + 4);
+    const f32x4 a2l = *reinterpret_cast<const f32x4*>(o2), a2h = *reinterpret_cast<const f32x4*>(o2 + 4);
+    const u32x4 yw = load16(dy);
+    float a1[8], a2[8], y[8], x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a1[i] = a1l[i]; a1[4 + i] = a1h[i];
+      a2[i] = a2l[i]; a2[4 + i] = a2h[i];
+      y[2 * i] = bf16_lo(yw[i]);
+      y[2 * i + 1] = bf16_hi(yw[i]);
+    }
+    float ss = 0.f, dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = a1[i] - lam * a2[i];
+      ss = fmaf(x[i], x[i], ss);
+      dot = fmaf(x[i], y[i], dot);
+    }
+    ss = row16_sum(ss);
+    dot = row16_sum(dot);
+    const float rr = rsqrtf(ss * (1.f / kDV) + p.eps);
+    const float k1 = p.g * rr, k2 = p.g * rr * rr * rr * dot * (1.f / kDV);
+    bf16x8 dq;
+    float e1 = 0.f, e2 = 0.f, g2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float d = k1 * y[i] - k2 * x[i];
+      dq[i] = (bf16)d;
+      // D_b from the rounded dO the MFMAs use, so that D_b equals the row sum of P_b * dP_b
+      // that they form (the softmax Jacobian's subtraction then cancels what it should)
+      const float dr = (float)dq[i];
+      e1 = fmaf(dr, a1[i], e1);
+      e2 = fmaf(dr, a2[i], e2);
+      g2 = fmaf(d, a2[i], g2);
+    }
+    e1 = row16_sum(e1);
+    e2 = row16_sum(e2);
+    g2 = row16_sum(g2);
+    if (row < p.N) {
+      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.d_o) + r * kDV + 8 * sub) = dq;
+      if (sub == 0) {
+        p.lse_d[2 * BHN + r] = e1;           // D_1
+        p.lse_d[3 * BHN + r] = -lam * e2;    // D_2
+        p.dl_row[r] = -g2;                   // this row's share of dlambda (unrounded dO)
+      }
+    }
   }
 }
 
@@ -196,7 +237,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   const int qt_wave = p.causal ? kw / kT : 0;       // first query tile with a row >= kw
   const bool wave_has_keys = kw < N;
 
-  auto compute = [&](int qt, int buf) {
+  // MASK: the tile holds a query before the diagonal or past N, or a key past N (wave-uniform)
+  auto compute = [&](int qt, int buf, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const bf16* st = smem + buf * STAGE;
     const int q0 = qt * kT;
     const float* rowd = reinterpret_cast<const float*>(st + 2 * QT + OT);  // [4][32]
@@ -219,7 +262,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
       x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[t], x, 0, 0, 0);
     }
     // P, dS (registers r: query q0 + 8 (r/4) + 4 hh + r % 4, key kw + c)
-    const int key = kw + c;
     const float dscale = br == 0 ? 1.f : -lam;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -229,12 +271,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * j + i;
-        const int q = q0 + ql + i;
-        const bool vis = q < N && key < N && (!p.causal || key <= q);
-        const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse[i])) : 0.f;
-        const float dp = dscale * x[r];
+        float e = fmaf(s[r], sl2, -lse[i]);
+        if constexpr (MASK) {
+          const int q = q0 + ql + i, key = kw + c;
+          const bool vis = q < N && key < N && (!p.causal || key <= q);
+          e = vis ? e : -INFINITY;           // exp2(-inf) = 0: a select, not a branch
+        }
+        const float pr = __builtin_amdgcn_exp2f(e);
         s[r] = pr * dscale;                 // P' = P (branch 1) or -lambda P (branch 2), for dV
-        x[r] = pr * (dp - dd[i]);           // dS
+        x[r] = pr * fmaf(dscale, x[r], -dd[i]);  // dS
       }
     }
     // dV^T += dO^T P', dK^T += Q^T dS (B operands: 16-row halves of the accumulators)
@@ -266,13 +311,24 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   issue_tile(qt_begin * kT, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int qt = qt_begin; qt < nq; ++qt) {
-    const int buf = (qt - qt_begin) & 1;
-    if (qt + 1 < nq) issue_tile((qt + 1) * kT, buf ^ 1);
-    if (wave_has_keys && qt >= qt_wave) compute(qt, buf);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
+  auto run = [&](int qa, int qb, auto mask_tag) {
+    for (int qt = qa; qt < qb; ++qt) {
+      const int buf = (qt - qt_begin) & 1;
+      if (qt + 1 < nq) issue_tile((qt + 1) * kT, buf ^ 1);
+      if (wave_has_keys && qt >= qt_wave) compute(qt, buf, mask_tag);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  };
+  // Tiles [fa, fb) need no mask for either wave: every query is at or past both waves' last key
+  // (the two diagonal tiles come before), every query row and key is inside N.  Separate loops
+  // keep the masked code out of the steady state.
+  const bool keys_full = key0 + 64 <= N;
+  const int fa = keys_full ? min(nq, p.causal ? qt_begin + 2 : qt_begin) : nq;
+  const int fb = keys_full ? max(fa, N / kT) : nq;
+  run(qt_begin, fa, std::true_type{});
+  run(fa, fb, std::false_type{});
+  run(fb, nq, std::true_type{});
 
   // ---- epilogue: branch-2 waves hand their dV part to the branch-1 waves; write dK_b, dV
   float* xb = reinterpret_cast<float*>(smem) + kh * (64 * 64);
@@ -400,7 +456,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   const int tcol = dh * 16 + 4 * (jj & 3);
   const float dscale = br == 0 ? 1.f : -lam;
 
-  auto compute = [&](int kt, int buf) {
+  // MASK: the tile holds a key past the diagonal or past N, or a row past N (wave-uniform)
+  auto compute = [&](int kt, int buf, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const bf16* st = smem + buf * STAGE;
     const int k0 = kt * kT;
     f32x16 s, x;
@@ -417,10 +475,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
     // registers r: key k0 + 8 (r/4) + 4 hh + r % 4; query qrow
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const bool vis = key < N && qrow < N && (!p.causal || key <= qrow);
-      const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse)) : 0.f;
-      s[r] = pr * (dscale * x[r] - dd);     // dS^T
+      float e = fmaf(s[r], sl2, -lse);
+      if constexpr (MASK) {
+        const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const bool vis = key < N && qrow < N && (!p.causal || key <= qrow);
+        e = vis ? e : -INFINITY;             // exp2(-inf) = 0: a select, not a branch
+      }
+      const float pr = __builtin_amdgcn_exp2f(e);
+      s[r] = pr * fmaf(dscale, x[r], -dd);  // dS^T
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -444,12 +506,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   issue_tile(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    if (kt + 1 < ntiles) issue_tile((kt + 1) * kT, (kt + 1) & 1);
-    if (kt < nt_wave) compute(kt, kt & 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
+  auto run = [&](int ka, int kb, auto mask_tag) {
+    for (int kt = ka; kt < kb; ++kt) {
+      if (kt + 1 < ntiles) issue_tile((kt + 1) * kT, (kt + 1) & 1);
+      if (kt < nt_wave) compute(kt, kt & 1, mask_tag);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  };
+  // Key tiles [0, fe) need no mask for either wave: all their keys precede both waves' first row
+  // (causal) and every row is inside N.  The diagonal and tail tiles run masked after them.
+  const int fe = row0 + 64 <= N ? (p.causal ? row0 / kT : N / kT) : 0;
+  run(0, fe, std::false_type{});
+  run(fe, ntiles, std::true_type{});
   if (!wave_has_rows || qrow >= N) return;
   float* dqp = (br == 0 ? p.dq1 : p.dq2) + ((int64_t)bh * N + qrow) * kD;
 #pragma unroll
@@ -463,16 +532,23 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dlambda per head and the four vector gradients (one wavefront per head)
-__global__ __launch_bounds__(64) void bwd_lambda_kernel(const BwdParams p) {
+// dlambda per head and the four vector gradients
+constexpr int kLambdaThreads = 1024;
+
+__global__ __launch_bounds__(kLambdaThreads) void bwd_lambda_kernel(const BwdParams p) {
+  __shared__ float part[kLambdaThreads / 64];
   const int h = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float s = 0.f;
   for (int b = 0; b < p.B; ++b) {
     const float* dl = p.dl_row + ((int64_t)b * p.H + h) * p.N;
-    for (int i = lane; i < p.N; i += 64) s += dl[i];
+    for (int i = tid; i < p.N; i += kLambdaThreads) s += dl[i];
   }
-  const float dlam = wave_sum(s);
+  s = wave_sum(s);
+  if (lane == 0) part[w] = s;
+  __syncthreads();
+  if (w != 0) return;
+  const float dlam = wave_sum(lane < kLambdaThreads / 64 ? part[lane] : 0.f);
   const LambdaArgs& L = p.lam;
   if (L.override_ != nullptr) return;  // lambda given directly: no vector gradients
   const int64_t base = (int64_t)h * L.dl;
@@ -494,7 +570,8 @@ __global__ __launch_bounds__(64) void bwd_lambda_kernel(const BwdParams p) {
 
 hipError_t launch_bwd_v1(const BwdParams& p, hipStream_t stream) {
   BwdParams q = p;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((p.N + 3) / 4, p.B * p.H), dim3(kThreads), 0, stream, q);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(p.B * p.H, (p.N + kPrepRowsPerBlock - 1) / kPrepRowsPerBlock),
+                     dim3(kThreads), 0, stream, q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   q.n_row_blocks = (p.N + 63) / 64;
@@ -502,7 +579,7 @@ hipError_t launch_bwd_v1(const BwdParams& p, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.B * p.H, q.n_row_blocks), dim3(kThreads), 0, stream, q);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_lambda_kernel, dim3(p.H), dim3(64), 0, stream, q);
+  hipLaunchKernelGGL(bwd_lambda_kernel, dim3(p.H), dim3(kLambdaThreads), 0, stream, q);
   return hipGetLastError();
 }
 

@@ -156,7 +156,9 @@ da_status diffattn_fwd_v2_window(da_tensor q1, da_tensor q2, da_tensor k, da_ten
  *   dlam->dlq1 .. dlk2  : fp32 [H, dl] (required unless lam->lambda_override is set, in which
  *                         case lambda is an input with no vector gradients)
  * workspace: at least diffattn_bwd_v1_workspace_bytes(B, H, N, d) bytes, 16-byte aligned.
- * Supported: d == 64, dtype DA_BF16, B * H * N < 2^28.
+ * Supported: d == 64, dtype DA_BF16, B * H * N < 2^28.  B, H or N == 0: DA_OK and nothing is
+ * written (no row contributes, so a caller that wants the lambda-vector gradients of an empty
+ * batch sets them to zero itself).
  */
 size_t diffattn_v1_train_stash_bytes(int32_t B, int32_t H, int32_t N, int32_t d);
 size_t diffattn_bwd_v1_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d);
