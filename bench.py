@@ -1,18 +1,22 @@
-"""Benchmark of the differential-attention forward path on one MI355X.
+"""Benchmark of the differential-attention hot path on one MI355X.
 
 A step is one pass of the hot path over one batch of seeded synthetic input already resident in
 HBM.  The headline workload is the V1 prefill at a 4K context (B=4, H=16, N=4096, d=64, V width
 128, causal, bf16 in / fp32 accumulate, layer 12); its line carries the MFMA roofline and the CPU
-oracle baseline.  The V2 prefill (B=2, 32 query heads / 16 pairs over 8 KV heads, D=128, N=8192)
-and the V2 decode step (B=64, 32 query / 8 KV heads, D=128, 32K-token cache) are reported in the
-same JSON line under "secondary", each with its own roofline.
+oracle baseline.  The same JSON line carries, under "secondary", each with its own roofline: the
+V2 prefill (B=2, 32 query heads / 16 pairs over 8 KV heads, D=128, N=8192), the V2 decode step
+(B=64, 32 query / 8 KV heads, D=128, 32K-token cache), the same decode over a paged cache with
+ragged lengths, the V1 prefill under a 1024-key sliding window, the V1-layout decode step, and
+the V1 backward at the 4K training shape.
 
 FLOP and byte conventions (per launch):
   V1 prefill  algorithmic flops  = B*H * 8*d * Np      (two QK^T products + one (A1-lambda A2)V)
               executed MFMA flops = B*H * 12*d * Np    (two QK^T + two P.V in one fused pass)
   V2 prefill  algorithmic flops  = B*P * 6*D * Np,  executed = B*P * 8*D * Np
   decode      algorithmic bytes  = K and V cache + queries + output (every byte read once)
-with Np = N(N+1)/2 causal query-key pairs.
+  V1 backward algorithmic flops  = B*H * 16*d * Np   (dO V^T, dV, and dQ_b, dK_b per branch)
+              executed MFMA flops = B*H * 40*d * Np  (scores and dO V^T formed in both kernels)
+with Np = N(N+1)/2 causal query-key pairs (the window's visible pairs for the sliding window).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
        [--only v1|v2|decode|decode_v1|swa|paged|bwd]
@@ -44,6 +48,7 @@ KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "prefill_bf16.hip"),
     "decode": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "decode_v2.hip"),
     "decode_v1": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "decode_v1.hip"),
+    "bwd": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "bwd_v1.hip"),
 }
 
 
@@ -303,7 +308,7 @@ def bench_bwd_v1(da, torch, steps, warmup):
                    "causal": True, "layer": layer, "dtype": "bf16 in, fp32 gradients"},
         "roofline": {"bound": "mfma", "achieved": round(tf_alg, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf_alg / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic("v1_backward_4k", "bwd"),
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
                      "kernel": "bwd_prep + bwd_dkdv + bwd_dq + bwd_lambda (whole backward)"},
