@@ -127,12 +127,15 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------------------------
 // dK_1, dK_2, dV: per 64 keys of a head
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
-  // per stage: Q_1, Q_2 [32][64] (K layout), dO [32][128] (V layout), LSE_1, LSE_2, D_1, D_2 [32]
+  // per stage: Q_1, Q_2 [32][64] (K layout), dO [32][128] twice -- in the V layout for the
+  // transposed reads of dV and in the 128-column K layout for the row-wise reads of dO V^T (one
+  // layout cannot serve both without bank conflicts or extra address registers) --, then
+  // LSE_1, LSE_2, D_1, D_2 [32]
   constexpr int QT = kT * kD;              // elements of one Q tile
-  constexpr int OT = kT * kDV;             // elements of the dO tile
+  constexpr int OT = kT * kDV;             // elements of one dO tile
   // + 1 KB for the row data: one wavefront DMA writes 64 x 16 bytes, of which the first 512 hold
   // LSE_1, LSE_2, D_1, D_2 (the rest read past the buffer's end and land as zeros)
-  constexpr int STAGE = 2 * QT + OT + 512;
+  constexpr int STAGE = 2 * QT + 2 * OT + 512;
   __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
   static_assert(2 * STAGE * 2 >= 2 * 64 * 64 * 4, "dV exchange must fit the tile buffers");
 
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   const char* q2_base = static_cast<const char*>(p.q2) + 2 * (b * p.sq2.sb + h * p.sq2.sh);
   const char* do_base = static_cast<const char*>(p.d_o) + (int64_t)bh * N * kDV * 2;
   int q_lrow;
-  uint32_t q_lchunk, o_lane[2];
+  uint32_t q_lchunk, o_lane[2], ok_lane[2];
   {
     const int e = 512 * w + 8 * lane;      // element of a Q tile this lane's 16 bytes land on
     q_lrow = e / kD;
@@ -188,6 +191,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
       const int slot = (ev & 127) >> 3;
       const int lcol = ((((slot >> 1) ^ (2 * (vrow & 3)))) << 4) + ((slot & 1) << 3);
       o_lane[i] = (uint32_t)vrow * (kDV * 2) + lcol * 2;
+      ok_lane[i] = (uint32_t)vrow * (kDV * 2) + (uint32_t)((slot ^ k_swz<kDV>(vrow)) << 4);
     }
   }
   const __amdgpu_buffer_rsrc_t r_ld = make_rsrc(p.lse_d, (uint32_t)(4 * BHN * 4));
@@ -201,13 +205,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(do_base + (size_t)q0 * kDV * 2, (uint32_t)rows_left * kDV * 2);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(ro, st + 2 * QT + 512 * (w + 4 * i), o_lane[i]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(ro, st + 2 * QT + OT + 512 * (w + 4 * i), ok_lane[i]);
     if (w == 0) {
       // lanes 0..31: 16 bytes of LSE_1, LSE_2, D_1, D_2 for rows q0 .. q0+31; the rest read past
       // the buffer's end and land as zeros
       const int k = lane >> 3, piece = lane & 7;
       const uint32_t off = lane < 32 ? (uint32_t)((((int64_t)k * BHN + (int64_t)bh * N + q0) * 4) + piece * 16)
                                      : (uint32_t)(4 * BHN * 4);
-      dma16(r_ld, st + 2 * QT + OT, off);
+      dma16(r_ld, st + 2 * QT + 2 * OT, off);
     }
   };
 
@@ -225,7 +231,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   // LDS read offsets (elements within a stage)
   //  A operand of S = Q K^T: Q row c, chunk 2t + hh
   const int q_rd = (br == 0 ? 0 : QT) + k_off<kD>(c, 8 * hh);  // chunk t: XOR 32 bytes * t
-  //  A operand of dO V^T: dO row c, 16-byte chunk 2t + hh (V layout)
+  const int o_rd = k_off<kDV>(c, 8 * hh);                          // dO row c, K-layout copy
+  //  A operand of dO V^T: dO row c, 16-byte chunk 2t + hh (the K-layout copy)
   //  transposed reads (dO^T, Q^T): lane j of a 16-lane group addresses row 4 hh + j / 4 (+ 16 u,
   //  + 8 upper), columns 32 blk + 16 dh + 4 (j % 4)
   const int jj = lane & 15, dh = (lane >> 4) & 1;
@@ -242,7 +249,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const bf16* st = smem + buf * STAGE;
     const int q0 = qt * kT;
-    const float* rowd = reinterpret_cast<const float*>(st + 2 * QT + OT);  // [4][32]
+    const float* rowd = reinterpret_cast<const float*>(st + 2 * QT + 2 * OT);  // [4][32]
+    __builtin_amdgcn_s_setprio(1);
     // S[q][key]
     f32x16 s;
 #pragma unroll
@@ -258,9 +266,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
     for (int r = 0; r < 16; ++r) x[r] = 0.f;
 #pragma unroll
     for (int t = 0; t < kDV / 16; ++t) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + 2 * QT + v_off(c, 16 * t + 8 * hh));
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + 2 * QT + OT + (o_rd ^ (16 * t)));
       x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[t], x, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // P, dS (registers r: query q0 + 8 (r/4) + 4 hh + r % 4, key kw + c)
     const float dscale = br == 0 ? 1.f : -lam;
 #pragma unroll
@@ -283,6 +292,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
       }
     }
     // dV^T += dO^T P', dK^T += Q^T dS (B operands: 16-row halves of the accumulators)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float dummy = 0.f;
@@ -305,6 +315,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
         dk[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), sb, dk[dbk], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- main loop over query tiles (tile t+1 loads during tile t)
@@ -428,8 +439,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
       const int ev = 512 * (w + 4 * i) + 8 * lane;
       const int vrow = ev >> 7;
       const int slot = (ev & 127) >> 3;
-      const int lcol = ((((slot >> 1) ^ (2 * (vrow & 3)))) << 4) + ((slot & 1) << 3);
-      v_lane[i] = (uint32_t)vrow * v_row + lcol * 2;
+      v_lane[i] = (uint32_t)vrow * v_row + (uint32_t)((slot ^ k_swz<kDV>(vrow)) << 4);
     }
   }
   auto issue_tile = [&](int k0, int buf) {
@@ -451,6 +461,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
     for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
 
   const int k_rd = (br == 0 ? 0 : KT) + k_off<kD>(c, 8 * hh);
+  // the V tile is only read row by row here, so it takes the 128-column K-tile layout, whose
+  // row-wise reads are free of bank conflicts
+  const int v_rd = k_off<kDV>(c, 8 * hh);
   const int jj = lane & 15, dh = (lane >> 4) & 1;
   const int trow = 4 * hh + (jj >> 2);
   const int tcol = dh * 16 + 4 * (jj & 3);
@@ -464,14 +477,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
     f32x16 s, x;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s[r] = 0.f; x[r] = 0.f; }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < kD / 16; ++t)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(st + (k_rd ^ (16 * t))), qf[t], s, 0, 0, 0);
 #pragma unroll
     for (int t = 0; t < kDV / 16; ++t) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + 2 * KT + v_off(c, 16 * t + 8 * hh));
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + 2 * KT + (v_rd ^ (16 * t)));
       x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, of[t], x, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // registers r: key k0 + 8 (r/4) + 4 hh + r % 4; query qrow
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -484,6 +499,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
       const float pr = __builtin_amdgcn_exp2f(e);
       s[r] = pr * fmaf(dscale, x[r], -dd);  // dS^T
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float dummy = 0.f;
@@ -497,6 +513,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
         dq[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), sb, dq[dbk], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   const int kv_end = p.causal ? min(N, row0 + 64) : N;
