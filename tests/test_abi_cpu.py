@@ -222,3 +222,62 @@ def test_binding_refuses_cpu_tensors(da):
     v = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         da.diffattn_fwd_v1(x, x, x, x, v, layer=1, out=v, lambda_override=None)
+
+
+def test_train_and_bwd_sizes(da):
+    # stash: O_1, O_2 [2, B, H, N, 2d] fp32, then LSE_1, LSE_2, D_1, D_2 [4, B, H, N] fp32
+    bhn = 2 * 3 * 100
+    assert da.diffattn_v1_train_stash_bytes(2, 3, 100, 64) == (2 * bhn * 128 + 4 * bhn) * 4
+    # workspace: dO bf16 [B, H, N, 2d], then the rows' dlambda shares fp32 [B, H, N]
+    assert da.diffattn_bwd_v1_workspace_bytes(2, 3, 100, 64) == bhn * 128 * 2 + bhn * 4
+    assert da.diffattn_v1_train_stash_bytes(1, 1, 8, 32) == 0
+    assert da.diffattn_bwd_v1_workspace_bytes(0, 1, 8, 64) == 0
+
+
+def test_train_and_bwd_host_validation(da):
+    lib = da.load_library()
+    t6 = [_t() for _ in range(6)]
+    lam = _lam(dl=64)
+    B, H, N = 1, 2, 40
+    stash = da.diffattn_v1_train_stash_bytes(B, H, N, 64)
+    ws = da.diffattn_bwd_v1_workspace_bytes(B, H, N, 64)
+
+    def train(st=0x40000, nbytes=stash, d=64, dt=1, n=N, eps=1e-5):
+        return lib.diffattn_fwd_v1_train(*t6, B, H, n, d, dt, ctypes.byref(lam), 1, eps, st, nbytes, None)
+
+    assert train(n=0) == 0                                   # empty: nothing enqueued
+    assert train(n=-1) == 2
+    assert train(dt=0) == 3                                  # the training path is bf16 only
+    assert train(d=128) == 3
+    assert train(st=None) == 4
+    assert train(nbytes=stash - 1) == 4
+    assert train(st=0x40008) == 4                            # misaligned stash
+
+    g = da_mod().DaLambdaGrad(0x50000, 0x50000, 0x50000, 0x50000)
+    grads = [0x60000] * 5
+
+    def bwd(gr=grads, lg=g, st=0x40000, sb=stash, w=0x70000, wb=ws, d=64, dt=1, n=N, eps=1e-5,
+            lm=lam):
+        return lib.diffattn_bwd_v1(*t6, *gr, B, H, n, d, dt, ctypes.byref(lm),
+                                   ctypes.byref(lg) if lg is not None else None, 1, eps, st, sb,
+                                   w, wb, None)
+
+    assert bwd(n=0) == 0
+    assert bwd(n=-3) == 2
+    assert bwd(dt=0) == 3
+    assert bwd(d=32) == 3
+    assert bwd(eps=float("nan")) == 2
+    assert bwd(gr=[0x60000, 0, 0x60000, 0x60000, 0x60000]) == 1     # missing dq2
+    assert bwd(gr=[0x60008] + [0x60000] * 4) == 1                    # misaligned dq1
+    assert bwd(lg=None) == 1                          # lambda vectors need their gradients
+    assert bwd(lg=da_mod().DaLambdaGrad(0x50000, None, 0x50000, 0x50000)) == 1
+    assert bwd(st=None) == 4
+    assert bwd(sb=stash - 16) == 4
+    assert bwd(w=None) == 4
+    assert bwd(wb=ws - 1) == 4
+    assert bwd(w=0x70008) == 4
+    assert bwd(lm=_lam(layer=0)) == 2
+    bad = list(t6)
+    bad[5] = _t(ptr=0)
+    assert lib.diffattn_bwd_v1(*bad, *grads, B, H, N, 64, 1, ctypes.byref(lam), ctypes.byref(g), 1,
+                               1e-5, 0x40000, stash, 0x70000, ws, None) == 1   # NULL dy
