@@ -12,11 +12,14 @@
 //   D_1  = dO . O_1,  D_2 = -lambda dO . O_2       (row-wise; O_b = A_b V from the forward)
 //   dQ_b = dS_b K_b / sqrt(d),  dK_b = dS_b^T Q_b / sqrt(d),
 //   dlambda = -sum(dO . O_2), and the four lambda vectors through the exponentials.
+// With c_1 = 1, c_2 = -lambda and Dt_b = dO . O_b, dS_b = c_b A_b * (dO V^T - Dt_b): the kernels
+// form A_b * (dO V^T - Dt_b), starting the dO V^T accumulator at -Dt_b, and apply c_b once to the
+// finished dQ_b, dK_b and branch-2 part of dV.
 //
 // Kernels (A_b is never stored: each kernel rebuilds the weights it needs from the scores and the
 // forward's base-2 log-sum-exp, P = exp2(s log2(e)/sqrt(d) - LSE)):
-//  * bwd_prep: 16 lanes per row: O, r, dO (stored bf16 for the MFMAs), D_1, D_2 and the row's
-//    share of dlambda.
+//  * bwd_prep: 16 lanes per row: O, r, dO (stored bf16 for the MFMAs), -Dt_1, -Dt_2 and the
+//    row's share of dlambda.
 //  * bwd_dkdv: one 256-thread workgroup per 64 keys of a head; its waves are (branch, 32-key
 //    half).  Each wave keeps its keys' K and V as MFMA operands in registers and streams 32-row
 //    query tiles (Q_1, Q_2, dO, LSE, D) through LDS: S = Q K^T, P, dO V^T, dS on 32x32x16 bf16
@@ -116,8 +119,10 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
     if (row < p.N) {
       *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.d_o) + r * kDV + 8 * sub) = dq;
       if (sub == 0) {
-        p.lse_d[2 * BHN + r] = e1;           // D_1
-        p.lse_d[3 * BHN + r] = -lam * e2;    // D_2
+        // minus the row terms without the branch factor: D_b = c_b * Dt_b with Dt_b = dO . O_b,
+        // c_1 = 1, c_2 = -lambda (the consumers start an accumulator at -Dt_b)
+        p.lse_d[2 * BHN + r] = -e1;
+        p.lse_d[3 * BHN + r] = -e2;
         p.dl_row[r] = -g2;                   // this row's share of dlambda (unrounded dO)
       }
     }
@@ -260,23 +265,27 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
       const int off = q_rd ^ (16 * t);  // elements: chunk 2t + hh, swizzle XOR on the chunk bits
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(st + off), kf[t], s, 0, 0, 0);
     }
-    // X[q][key] = dO V^T
+    // X[q][key] = dO V^T - Dt_b[q]: the accumulator starts at -Dt_b (stored negated, one value per
+    // query row, in the accumulator's row order)
     f32x16 x;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = 0.f;
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 nd = *reinterpret_cast<const f32x4*>(rowd + (2 + br) * kT + 8 * j + 4 * hh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * j + i] = nd[i];
+    }
 #pragma unroll
     for (int t = 0; t < kDV / 16; ++t) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + 2 * QT + OT + (o_rd ^ (16 * t)));
       x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[t], x, 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
-    // P, dS (registers r: query q0 + 8 (r/4) + 4 hh + r % 4, key kw + c)
-    const float dscale = br == 0 ? 1.f : -lam;
+    // P_b and dS_b / c_b = P_b (X - Dt_b) (registers r: query q0 + 8 (r/4) + 4 hh + r % 4, key
+    // kw + c); the branch factor c_b multiplies dK_b and this wave's dV part at the end
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ql = 8 * j + 4 * hh;
       const f32x4 lse = *reinterpret_cast<const f32x4*>(rowd + br * kT + ql);
-      const f32x4 dd = *reinterpret_cast<const f32x4*>(rowd + (2 + br) * kT + ql);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * j + i;
@@ -287,11 +296,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
           e = vis ? e : -INFINITY;           // exp2(-inf) = 0: a select, not a branch
         }
         const float pr = __builtin_amdgcn_exp2f(e);
-        s[r] = pr * dscale;                 // P' = P (branch 1) or -lambda P (branch 2), for dV
-        x[r] = pr * fmaf(dscale, x[r], -dd[i]);  // dS
+        s[r] = pr;
+        x[r] = pr * x[r];
       }
     }
-    // dV^T += dO^T P', dK^T += Q^T dS (B operands: 16-row halves of the accumulators)
+    // dV^T += dO^T P_b, dK^T += Q^T dS_b / c_b (B operands: 16-row halves of the accumulators)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -341,23 +350,26 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   run(fa, fb, std::false_type{});
   run(fb, nq, std::true_type{});
 
-  // ---- epilogue: branch-2 waves hand their dV part to the branch-1 waves; write dK_b, dV
+  // ---- epilogue: branch-2 waves hand their dV part (times c_2 = -lambda) to the branch-1 waves;
+  // write dK_b (times c_b / sqrt(d)) and dV
+  const float cb = br == 0 ? 1.f : -lam;
   float* xb = reinterpret_cast<float*>(smem) + kh * (64 * 64);
   if (br == 1) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xb[(db * 16 + r) * 64 + lane] = dv[db][r];
+      for (int r = 0; r < 16; ++r) xb[(db * 16 + r) * 64 + lane] = cb * dv[db][r];
   }
   const int key = kw + c;
   if (wave_has_keys && key < N) {
     float* dkp = (br == 0 ? p.dk1 : p.dk2) + ((int64_t)bh * N + key) * kD;
+    const float ks = cb * p.scale;
 #pragma unroll
     for (int dbk = 0; dbk < 2; ++dbk)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 v4 = {dk[dbk][4 * j] * p.scale, dk[dbk][4 * j + 1] * p.scale,
-                          dk[dbk][4 * j + 2] * p.scale, dk[dbk][4 * j + 3] * p.scale};
+        const f32x4 v4 = {dk[dbk][4 * j] * ks, dk[dbk][4 * j + 1] * ks,
+                          dk[dbk][4 * j + 2] * ks, dk[dbk][4 * j + 3] * ks};
         *reinterpret_cast<f32x4*>(dkp + dbk * 32 + 8 * j + 4 * hh) = v4;
       }
   }
@@ -401,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
 
   // Q_b^T and dO^T as B operands: lane n = query wrow + c, k = 16 t + 8 hh .. + 7
   bf16x8 qf[kD / 16], of[kDV / 16];
-  float lse = 0.f, dd = 0.f;
+  float lse = 0.f, ndd = 0.f;  // this lane's row: LSE_b and -Dt_b
   {
     const bf16* qb = static_cast<const bf16*>(br == 0 ? p.q1 : p.q2) +
                      b * (br == 0 ? p.sq1.sb : p.sq2.sb) + h * (br == 0 ? p.sq1.sh : p.sq2.sh);
@@ -417,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
       of[t] = __builtin_bit_cast(bf16x8, bload16(ro, (uint32_t)(qrow * kDV * 2) + 32 * t + 16 * hh));
     if (qrow < N) {
       lse = p.lse_d[(int64_t)br * BHN + (int64_t)bh * N + qrow];
-      dd = p.lse_d[(int64_t)(2 + br) * BHN + (int64_t)bh * N + qrow];
+      ndd = p.lse_d[(int64_t)(2 + br) * BHN + (int64_t)bh * N + qrow];
     }
     __builtin_amdgcn_s_waitcnt(0);
   }
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   const int jj = lane & 15, dh = (lane >> 4) & 1;
   const int trow = 4 * hh + (jj >> 2);
   const int tcol = dh * 16 + 4 * (jj & 3);
-  const float dscale = br == 0 ? 1.f : -lam;
+  const float cb = br == 0 ? 1.f : -lam;  // branch factor, applied to dQ_b at the end
 
   // MASK: the tile holds a key past the diagonal or past N, or a row past N (wave-uniform)
   auto compute = [&](int kt, int buf, auto mask_tag) {
@@ -497,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
         e = vis ? e : -INFINITY;             // exp2(-inf) = 0: a select, not a branch
       }
       const float pr = __builtin_amdgcn_exp2f(e);
-      s[r] = pr * fmaf(dscale, x[r], -dd);  // dS^T
+      s[r] = pr * (x[r] + ndd);             // dS_b^T / c_b
     }
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -542,8 +554,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   for (int dbk = 0; dbk < 2; ++dbk)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const f32x4 v4 = {dq[dbk][4 * j] * p.scale, dq[dbk][4 * j + 1] * p.scale,
-                        dq[dbk][4 * j + 2] * p.scale, dq[dbk][4 * j + 3] * p.scale};
+      const float qs = cb * p.scale;
+      const f32x4 v4 = {dq[dbk][4 * j] * qs, dq[dbk][4 * j + 1] * qs,
+                        dq[dbk][4 * j + 2] * qs, dq[dbk][4 * j + 3] * qs};
       *reinterpret_cast<f32x4*>(dqp + dbk * 32 + 8 * j + 4 * hh) = v4;
     }
 }
