@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
     }
   }
   const __amdgpu_buffer_rsrc_t r_ld = make_rsrc(p.lse_d, (uint32_t)(4 * BHN * 4));
-  auto issue_tile = [&](int q0, int buf) {
+  auto issue_tile = [&](int q0, int buf) __attribute__((always_inline)) {
     bf16* st = smem + buf * STAGE;
     const int rows_left = N - q0;
     const __amdgpu_buffer_rsrc_t r1 = make_rsrc(q1_base + (size_t)q0 * q1_row, (uint32_t)rows_left * q1_row);
@@ -250,9 +250,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   const bool wave_has_keys = kw < N;
 
   // MASK: the tile holds a query before the diagonal or past N, or a key past N (wave-uniform)
-  auto compute = [&](int qt, int buf, auto mask_tag) {
+  // BUF: the stage buffer, a compile-time constant so that every LDS address is a loop-invariant
+  // register plus the instruction's immediate offset
+  auto compute = [&](int qt, auto buf_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const bf16* st = smem + buf * STAGE;
+    const bf16* st = smem + decltype(buf_tag)::value * STAGE;
     const int q0 = qt * kT;
     const float* rowd = reinterpret_cast<const float*>(st + 2 * QT + 2 * OT);  // [4][32]
     __builtin_amdgcn_s_setprio(1);
@@ -331,14 +333,23 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   issue_tile(qt_begin * kT, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  auto run = [&](int qa, int qb, auto mask_tag) {
-    for (int qt = qa; qt < qb; ++qt) {
-      const int buf = (qt - qt_begin) & 1;
-      if (qt + 1 < nq) issue_tile((qt + 1) * kT, buf ^ 1);
-      if (wave_has_keys && qt >= qt_wave) compute(qt, buf, mask_tag);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+  // one query tile: tile qt sits in buffer (qt - qt_begin) & 1 while the next one loads into the
+  // other; the loop runs two tiles per iteration so that the buffer index is known at compile time
+  auto step = [&](int qt, auto buf_tag, auto mask_tag) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (qt + 1 < nq) issue_tile((qt + 1) * kT, BUF ^ 1);
+    if (wave_has_keys && qt >= qt_wave) compute(qt, buf_tag, mask_tag);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  auto run = [&](int qa, int qb, auto mask_tag) __attribute__((always_inline)) {
+    int qt = qa;
+    if (qt < qb && ((qt - qt_begin) & 1) != 0) step(qt++, std::integral_constant<int, 1>{}, mask_tag);
+    for (; qt + 1 < qb; qt += 2) {
+      step(qt, std::integral_constant<int, 0>{}, mask_tag);
+      step(qt + 1, std::integral_constant<int, 1>{}, mask_tag);
     }
+    if (qt < qb) step(qt, std::integral_constant<int, 0>{}, mask_tag);
   };
   // Tiles [fa, fb) need no mask for either wave: every query is at or past both waves' last key
   // (the two diagonal tiles come before), every query row and key is inside N.  Separate loops
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
       v_lane[i] = (uint32_t)vrow * v_row + (uint32_t)((slot ^ k_swz<kDV>(vrow)) << 4);
     }
   }
-  auto issue_tile = [&](int k0, int buf) {
+  auto issue_tile = [&](int k0, int buf) __attribute__((always_inline)) {
     bf16* st = smem + buf * STAGE;
     const int rows_left = N - k0;
     const __amdgpu_buffer_rsrc_t r1 = make_rsrc(k1_base + (size_t)k0 * k1_row, (uint32_t)rows_left * k1_row);
@@ -482,9 +493,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   const float cb = br == 0 ? 1.f : -lam;  // branch factor, applied to dQ_b at the end
 
   // MASK: the tile holds a key past the diagonal or past N, or a row past N (wave-uniform)
-  auto compute = [&](int kt, int buf, auto mask_tag) {
+  // BUF: the stage buffer, a compile-time constant (see the dK/dV kernel)
+  auto compute = [&](int kt, auto buf_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const bf16* st = smem + buf * STAGE;
+    const bf16* st = smem + decltype(buf_tag)::value * STAGE;
     const int k0 = kt * kT;
     f32x16 s, x;
 #pragma unroll
@@ -535,13 +547,22 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   issue_tile(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  auto run = [&](int ka, int kb, auto mask_tag) {
-    for (int kt = ka; kt < kb; ++kt) {
-      if (kt + 1 < ntiles) issue_tile((kt + 1) * kT, (kt + 1) & 1);
-      if (kt < nt_wave) compute(kt, kt & 1, mask_tag);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+  // key tile kt sits in buffer kt & 1; two tiles per iteration keep the buffer index static
+  auto step = [&](int kt, auto buf_tag, auto mask_tag) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (kt + 1 < ntiles) issue_tile((kt + 1) * kT, BUF ^ 1);
+    if (kt < nt_wave) compute(kt, buf_tag, mask_tag);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  auto run = [&](int ka, int kb, auto mask_tag) __attribute__((always_inline)) {
+    int kt = ka;
+    if (kt < kb && (kt & 1) != 0) step(kt++, std::integral_constant<int, 1>{}, mask_tag);
+    for (; kt + 1 < kb; kt += 2) {
+      step(kt, std::integral_constant<int, 0>{}, mask_tag);
+      step(kt + 1, std::integral_constant<int, 1>{}, mask_tag);
     }
+    if (kt < kb) step(kt, std::integral_constant<int, 0>{}, mask_tag);
   };
   // Key tiles [0, fe) need no mask for either wave: all their keys precede both waves' first row
   // (causal) and every row is inside N.  The diagonal and tail tiles run masked after them.
