@@ -50,7 +50,8 @@ def diff_attn_v1_backward(q1, q2, k1, k2, v, lvecs, layer: int, dy, causal: bool
 
     q1, q2, k1, k2 [B, H, N, d]; v, dy [B, H, N, 2d]; lvecs = (lq1, lk1, lq2, lk2), each [H, dl].
     Returns a dict with dq1, dq2, dk1, dk2, dv (input shapes), dlam [H] and dlq1, dlk1, dlq2,
-    dlk2 ([H, dl]), all float64.
+    dlk2 ([H, dl]), all float64, and dlam_terms [H] = sum over rows and channels of |dO * O_2|,
+    the magnitude of dlam's terms before they cancel (an error scale for comparisons).
     """
     q1, q2, k1, k2, v, dy = (np.asarray(a, dtype=np.float64) for a in (q1, q2, k1, k2, v, dy))
     lq1, lk1, lq2, lk2 = (np.asarray(a, dtype=np.float64) for a in lvecs)
@@ -66,6 +67,7 @@ def diff_attn_v1_backward(q1, q2, k1, k2, v, lvecs, layer: int, dy, causal: bool
     out = {k: np.zeros_like(x) for k, x in (("dq1", q1), ("dq2", q2), ("dk1", k1), ("dk2", k2),
                                             ("dv", v))}
     dlam = np.zeros(H)
+    dlam_terms = np.zeros(H)
     for b in range(B):
         for h in range(H):
             a1 = softmax_rows(q1[b, h] @ k1[b, h].T * c, vis)
@@ -84,7 +86,10 @@ def diff_attn_v1_backward(q1, q2, k1, k2, v, lvecs, layer: int, dy, causal: bool
                 out[dq][b, h] = c * (ds @ kk[b, h])
                 out[dk][b, h] = c * (ds.T @ qq[b, h])
             dlam[h] += -np.sum(do * o2)
+            dlam_terms[h] += np.sum(np.abs(do * o2))
     out["dlam"] = dlam
+    # the size of dlambda's terms before they cancel: the scale its rounding error is set by
+    out["dlam_terms"] = dlam_terms
     out["dlq1"] = (dlam * ea)[:, None] * lk1
     out["dlk1"] = (dlam * ea)[:, None] * lq1
     out["dlq2"] = -(dlam * eb)[:, None] * lk2
