@@ -49,7 +49,7 @@ __device__ __forceinline__ float lam_of(const BwdParams& p, int h, int lane) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// prep: dO through the norm, D_b, dlambda shares
+// prep: dO through the norm, -Dt_b, dlambda shares
 // 16 lanes per row (8 of its 2d channels each), four rows per wavefront pass, two passes
 constexpr int kPrepRowsPerWave = 8;
 constexpr int kPrepRowsPerBlock = kPrepRowsPerWave * (kThreads / 64);
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
     for (int i = 0; i < 8; ++i) {
       const float d = k1 * y[i] - k2 * x[i];
       dq[i] = (bf16)d;
-      // D_b from the rounded dO the MFMAs use, so that D_b equals the row sum of P_b * dP_b
+      // Dt_b from the rounded dO the MFMAs use, so that c_b Dt_b equals the row sum of P_b * dP_b
       // that they form (the softmax Jacobian's subtraction then cancels what it should)
       const float dr = (float)dq[i];
       e1 = fmaf(dr, a1[i], e1);
@@ -135,11 +135,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   // per stage: Q_1, Q_2 [32][64] (K layout), dO [32][128] twice -- in the V layout for the
   // transposed reads of dV and in the 128-column K layout for the row-wise reads of dO V^T (one
   // layout cannot serve both without bank conflicts or extra address registers) --, then
-  // LSE_1, LSE_2, D_1, D_2 [32]
+  // LSE_1, LSE_2, -Dt_1, -Dt_2 [32]
   constexpr int QT = kT * kD;              // elements of one Q tile
   constexpr int OT = kT * kDV;             // elements of one dO tile
   // + 1 KB for the row data: one wavefront DMA writes 64 x 16 bytes, of which the first 512 hold
-  // LSE_1, LSE_2, D_1, D_2 (the rest read past the buffer's end and land as zeros)
+  // LSE_1, LSE_2, -Dt_1, -Dt_2 (the rest read past the buffer's end and land as zeros)
   constexpr int STAGE = 2 * QT + 2 * OT + 512;
   __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
   static_assert(2 * STAGE * 2 >= 2 * 64 * 64 * 4, "dV exchange must fit the tile buffers");
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(ro, st + 2 * QT + OT + 512 * (w + 4 * i), ok_lane[i]);
     if (w == 0) {
-      // lanes 0..31: 16 bytes of LSE_1, LSE_2, D_1, D_2 for rows q0 .. q0+31; the rest read past
+      // lanes 0..31: 16 bytes of LSE_1, LSE_2, -Dt_1, -Dt_2 for rows q0 .. q0+31; the rest read past
       // the buffer's end and land as zeros
       const int k = lane >> 3, piece = lane & 7;
       const uint32_t off = lane < 32 ? (uint32_t)((((int64_t)k * BHN + (int64_t)bh * N + q0) * 4) + piece * 16)

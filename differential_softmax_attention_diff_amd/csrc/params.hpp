@@ -71,7 +71,7 @@ struct BwdParams {
   float eps;
   float g;               // 1 - lambda_init
   const float* stash_o;  // [2, B, H, N, 2d] from the training forward
-  float* lse_d;          // [4, B, H, N]: LSE_1, LSE_2 (forward, base 2), D_1, D_2 (prep)
+  float* lse_d;          // [4, B, H, N]: LSE_1, LSE_2 (forward, base 2), -Dt_1, -Dt_2 (prep)
   void* d_o;             // [B, H, N, 2d] bf16: upstream gradient through the norm (prep)
   float* dl_row;         // [B, H, N]: each row's share of dlambda (prep)
   LambdaArgs lam;
