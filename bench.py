@@ -7,7 +7,7 @@ oracle baseline.  The same JSON line carries, under "secondary", each with its o
 V2 prefill (B=2, 32 query heads / 16 pairs over 8 KV heads, D=128, N=8192), the V2 decode step
 (B=64, 32 query / 8 KV heads, D=128, 32K-token cache), the same decode over a paged cache with
 ragged lengths, the V1 prefill under a 1024-key sliding window, the V1-layout decode step, and
-the V1 backward at the 4K training shape.
+the V1 backward at the 4K training shape, causal and under the same window.
 
 FLOP and byte conventions (per launch):
   V1 prefill  algorithmic flops  = B*H * 8*d * Np      (two QK^T products + one (A1-lambda A2)V)
@@ -19,7 +19,7 @@ FLOP and byte conventions (per launch):
 with Np = N(N+1)/2 causal query-key pairs (the window's visible pairs for the sliding window).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
-       [--only v1|v2|decode|decode_v1|swa|paged|bwd]
+       [--only v1|v2|decode|decode_v1|swa|paged|bwd|bwd_swa]
        [--no-cpu-baseline] [--cpu-seconds S]
 """
 
@@ -277,23 +277,25 @@ def bench_decode_v1(da, torch, steps, warmup):
     }
 
 
-def bench_bwd_v1(da, torch, steps, warmup):
-    """V1 backward at the 4K prefill shape: the training forward fills the stash once, then the
-    backward (prep, dK/dV, dQ and lambda kernels) is timed."""
-    cfg, t = wl.make("v1_prefill_4k")
+def bench_bwd_v1(da, torch, steps, warmup, window=0):
+    """V1 backward at the 4K prefill shape (optionally under the 1024-key sliding window of the
+    window workload): the training forward fills the stash once, then the backward (prep, dK/dV,
+    dQ and lambda kernels) is timed."""
+    name = "v1_swa_backward_4k" if window else "v1_backward_4k"
+    cfg, t = wl.make("v1_swa_4k" if window else "v1_prefill_4k")
     layer = cfg["layers"][0]
     B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
     args = [to_dev(t[k], torch) for k in ("q1", "q2", "k1", "k2", "v")]
     lv = [torch.from_numpy(x).to("cuda") for x in t["lambda"][layer]]
     rng = np.random.default_rng(77)
     dy = to_dev(wl.f32_to_bf16_bits(rng.standard_normal((B, H, N, 2 * d), dtype=np.float32)), torch)
-    _, stash = da.diffattn_fwd_v1_train(*args, *lv, layer=layer)
+    _, stash = da.diffattn_fwd_v1_train(*args, *lv, layer=layer, window=window)
     ws = torch.empty(da.diffattn_bwd_v1_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
-    grads = da.diffattn_bwd_v1(*args, dy, *lv, layer=layer, stash=stash, workspace=ws)
+    grads = da.diffattn_bwd_v1(*args, dy, *lv, layer=layer, stash=stash, workspace=ws, window=window)
     fn = lambda: da.diffattn_bwd_v1(*args, dy, *lv, layer=layer, stash=stash, workspace=ws,
-                                    grads=grads)
+                                    grads=grads, window=window)
     ms = time_launches(fn, steps, warmup, torch)
-    npairs = causal_pairs(N)
+    npairs = window_pairs(N, window) if window else causal_pairs(N)
     # gradient products: dP = dO V^T and dV = (A1 - lambda A2)^T dO (2d wide, once each), and
     # dQ_b = dS_b K_b, dK_b = dS_b^T Q_b per branch
     f_alg = B * H * 16 * d * npairs
@@ -303,12 +305,13 @@ def bench_bwd_v1(da, torch, steps, warmup):
     tf_alg = f_alg / (ms * 1e-3) / 1e12
     tf_exec = f_exec / (ms * 1e-3) / 1e12
     return {
-        "workload": "v1_backward_4k", "ms": ms, "value": round(tf_alg, 2), "unit": "TFLOP/s",
-        "config": {"workload": "v1_backward_4k", "B": B, "H": H, "N": N, "d": d, "dv": 2 * d,
-                   "causal": True, "layer": layer, "dtype": "bf16 in, fp32 gradients"},
+        "workload": name, "ms": ms, "value": round(tf_alg, 2), "unit": "TFLOP/s",
+        "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "dv": 2 * d,
+                   "causal": True, "window": window, "layer": layer,
+                   "dtype": "bf16 in, fp32 gradients"},
         "roofline": {"bound": "mfma", "achieved": round(tf_alg, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf_alg / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("v1_backward_4k", "bwd"),
+                     "traffic": measured_traffic(name, "bwd"),
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
                      "kernel": "bwd_prep + bwd_dkdv + bwd_dq + bwd_lambda (whole backward)"},
@@ -361,7 +364,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)  # clocks settle after ~20-50 ms of load
-    ap.add_argument("--only", choices=["v1", "v2", "decode", "decode_v1", "swa", "paged", "bwd"],
+    ap.add_argument("--only", choices=["v1", "v2", "decode", "decode_v1", "swa", "paged", "bwd", "bwd_swa"],
                     default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -416,6 +419,11 @@ def main():
     if a.only in (None, "bwd"):
         print("[bench] v1 backward", file=sys.stderr, flush=True)
         secondary.append(bench_bwd_v1(da, torch, a.steps, a.warmup))
+        torch.cuda.empty_cache()
+    if a.only in (None, "bwd_swa"):
+        print("[bench] v1 backward, sliding window", file=sys.stderr, flush=True)
+        cfg_w = wl.CONFIGS["v1_swa_4k"]
+        secondary.append(bench_bwd_v1(da, torch, a.steps, a.warmup, window=cfg_w["window"]))
         torch.cuda.empty_cache()
     if a.only == "v1" or a.only is None:
         print("[bench] v1 prefill", file=sys.stderr, flush=True)

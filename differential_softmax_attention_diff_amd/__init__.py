@@ -102,10 +102,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.diffattn_v1_train_stash_bytes.restype = sz
     lib.diffattn_bwd_v1_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.diffattn_bwd_v1_workspace_bytes.restype = sz
-    lib.diffattn_fwd_v1_train.argtypes = [T, T, T, T, T, T, i32, i32, i32, i32, i32, L, i32, f32, vp, sz, vp]
+    lib.diffattn_fwd_v1_train.argtypes = [T, T, T, T, T, T, i32, i32, i32, i32, i32, L, i32, i32, f32, vp,
+                                          sz, vp]
     lib.diffattn_fwd_v1_train.restype = i32
     lib.diffattn_bwd_v1.argtypes = [T, T, T, T, T, T, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, L,
-                                    ctypes.POINTER(DaLambdaGrad), i32, f32, vp, sz, vp, sz, vp]
+                                    ctypes.POINTER(DaLambdaGrad), i32, i32, f32, vp, sz, vp, sz, vp]
     lib.diffattn_bwd_v1.restype = i32
     lib.diffattn_decode_v1_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.diffattn_decode_v1_workspace_bytes.restype = sz
@@ -411,8 +412,8 @@ def diffattn_bwd_v1_workspace_bytes(B, H, N, d) -> int:
 
 
 def diffattn_fwd_v1_train(q1, q2, k1, k2, v, lq1=None, lk1=None, lq2=None, lk2=None, layer=1, *,
-                          out=None, causal=True, eps=1e-5, stash=None, lambda_override=None,
-                          lambda_out=None, stream=None):
+                          out=None, causal=True, window=0, eps=1e-5, stash=None,
+                          lambda_override=None, lambda_out=None, stream=None):
     """V1 forward (bf16) that also fills the stash the backward pass reads; returns (out, stash).
     ``stash`` is a GPU byte tensor of at least ``diffattn_v1_train_stash_bytes`` bytes."""
     torch = _torch()
@@ -432,13 +433,13 @@ def diffattn_fwd_v1_train(q1, q2, k1, k2, v, lq1=None, lk1=None, lq2=None, lk2=N
     with torch.cuda.device(q1.device):
         st = _stream(q1.device, stream)
         _check(load_library().diffattn_fwd_v1_train(
-            *descs, B, H, N, d, dt, ctypes.byref(lam), 1 if causal else 0, float(eps),
+            *descs, B, H, N, d, dt, ctypes.byref(lam), 1 if causal else 0, int(window), float(eps),
             stash.data_ptr(), stash.numel() * stash.element_size(), st), "diffattn_fwd_v1_train")
     return out, stash
 
 
 def diffattn_bwd_v1(q1, q2, k1, k2, v, dy, lq1=None, lk1=None, lq2=None, lk2=None, layer=1, *,
-                    stash, causal=True, eps=1e-5, workspace=None, grads=None,
+                    stash, causal=True, window=0, eps=1e-5, workspace=None, grads=None,
                     lambda_override=None, stream=None):
     """Gradients of the V1 output for upstream gradient dy [B, H, N, 2d] (bf16).  Returns a dict
     of fp32 GPU tensors: dq1, dq2, dk1, dk2 [B, H, N, d], dv [B, H, N, 2d] and (unless
@@ -473,7 +474,8 @@ def diffattn_bwd_v1(q1, q2, k1, k2, v, dy, lq1=None, lk1=None, lq2=None, lk2=Non
         st = _stream(dev, stream)
         _check(load_library().diffattn_bwd_v1(
             *descs, *(grads[k].data_ptr() for k in ("dq1", "dq2", "dk1", "dk2", "dv")),
-            B, H, N, d, dt, ctypes.byref(lam), ctypes.byref(lg), 1 if causal else 0, float(eps),
+            B, H, N, d, dt, ctypes.byref(lam), ctypes.byref(lg), 1 if causal else 0, int(window),
+            float(eps),
             stash.data_ptr(), stash.numel() * stash.element_size(), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), st), "diffattn_bwd_v1")
     return grads

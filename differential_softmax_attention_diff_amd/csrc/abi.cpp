@@ -277,15 +277,17 @@ size_t diffattn_bwd_v1_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t 
 da_status diffattn_fwd_v1_train(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2,
                                 da_tensor v, da_tensor out, int32_t B, int32_t H, int32_t N,
                                 int32_t d, da_dtype dtype, const da_lambda* lam, int32_t causal,
-                                float eps, void* stash, size_t stash_bytes, void* stream) {
-  if (B < 0 || H < 0 || N < 0) return DA_ERR_SHAPE;
+                                int32_t window, float eps, void* stash, size_t stash_bytes,
+                                void* stream) {
+  if (B < 0 || H < 0 || N < 0 || window < 0) return DA_ERR_SHAPE;
+  if (window > 0 && !causal) return DA_ERR_SHAPE;  // the window is a causal one
   if (B == 0 || H == 0 || N == 0) return DA_OK;
   if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
   if (d != 64) return d <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
   if ((int64_t)B * H * N * 16 >= ((int64_t)1 << 32)) return DA_ERR_UNSUPPORTED;
   const size_t need = diffattn_v1_train_stash_bytes(B, H, N, d);
   if (stash == nullptr || !aligned16(stash) || stash_bytes < need) return DA_ERR_WORKSPACE;
-  return fwd_v1(q1, q2, k1, k2, v, out, B, H, N, d, dtype, lam, causal, 0, eps, 0u, stream,
+  return fwd_v1(q1, q2, k1, k2, v, out, B, H, N, d, dtype, lam, causal, window, eps, 0u, stream,
                 static_cast<float*>(stash));
 }
 
@@ -293,9 +295,10 @@ da_status diffattn_bwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2
                           da_tensor dy, float* dq1, float* dq2, float* dk1, float* dk2, float* dv,
                           int32_t B, int32_t H, int32_t N, int32_t d, da_dtype dtype,
                           const da_lambda* lam, const da_lambda_grad* dlam, int32_t causal,
-                          float eps, const void* stash, size_t stash_bytes, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  if (B < 0 || H < 0 || N < 0) return DA_ERR_SHAPE;
+                          int32_t window, float eps, const void* stash, size_t stash_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || window < 0) return DA_ERR_SHAPE;
+  if (window > 0 && !causal) return DA_ERR_SHAPE;
   if (B == 0 || H == 0 || N == 0) return DA_OK;
   if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
   if (d != 64) return d <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
@@ -328,6 +331,7 @@ da_status diffattn_bwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2
   p.dq1 = dq1; p.dq2 = dq2; p.dk1 = dk1; p.dk2 = dk2; p.dv = dv;
   p.B = B; p.H = H; p.N = N;
   p.causal = causal ? 1 : 0;
+  p.window = window >= N ? 0 : window;  // a window covering every row is plain causal
   p.scale = (float)(1.0 / std::sqrt((double)d));
   p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   p.eps = eps;

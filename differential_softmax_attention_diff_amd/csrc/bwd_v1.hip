@@ -244,9 +244,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   const int trow = 4 * hh + (jj >> 2);
   const int tcol = dh * 16 + 4 * (jj & 3);
 
-  const int nq = (N + kT - 1) / kT;
-  const int qt_begin = p.causal ? key0 / kT : 0;    // first query tile the workgroup needs
+  // query tiles the workgroup needs: from the first row at or past its first key (causal) to the
+  // last row inside the window of its last key; each wave has its own sub-range
+  const int W = p.window;                           // causal sliding window (0: none)
+  const int qt_begin = p.causal ? key0 / kT : 0;
+  const int nq = W > 0 ? min((N + kT - 1) / kT, (key0 + 63 + W - 1) / kT + 1) : (N + kT - 1) / kT;
   const int qt_wave = p.causal ? kw / kT : 0;       // first query tile with a row >= kw
+  const int qt_wave_end = W > 0 ? (kw + 31 + W - 1) / kT + 1 : nq;  // past its last one
   const bool wave_has_keys = kw < N;
 
   // MASK: the tile holds a query before the diagonal or past N, or a key past N (wave-uniform)
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
         float e = fmaf(s[r], sl2, -lse[i]);
         if constexpr (MASK) {
           const int q = q0 + ql + i, key = kw + c;
-          const bool vis = q < N && key < N && (!p.causal || key <= q);
+          const bool vis = q < N && key < N && (!p.causal || key <= q) && (W == 0 || q - key < W);
           e = vis ? e : -INFINITY;           // exp2(-inf) = 0: a select, not a branch
         }
         const float pr = __builtin_amdgcn_exp2f(e);
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   auto step = [&](int qt, auto buf_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
     if (qt + 1 < nq) issue_tile((qt + 1) * kT, BUF ^ 1);
-    if (wave_has_keys && qt >= qt_wave) compute(qt, buf_tag, mask_tag);
+    if (wave_has_keys && qt >= qt_wave && qt < qt_wave_end) compute(qt, buf_tag, mask_tag);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -354,9 +358,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   // Tiles [fa, fb) need no mask for either wave: every query is at or past both waves' last key
   // (the two diagonal tiles come before), every query row and key is inside N.  Separate loops
   // keep the masked code out of the steady state.
+  // With a window, a tile is also whole only while its last row is inside the window of the
+  // workgroup's first key: q0 + 31 - key0 < W.
   const bool keys_full = key0 + 64 <= N;
   const int fa = keys_full ? min(nq, p.causal ? qt_begin + 2 : qt_begin) : nq;
-  const int fb = keys_full ? max(fa, N / kT) : nq;
+  int fb = keys_full ? max(fa, N / kT) : nq;
+  if (W > 0) fb = max(fa, min(fb, key0 + W - kT >= 0 ? (key0 + W - kT) / kT + 1 : 0));
   run(qt_begin, fa, std::true_type{});
   run(fa, fb, std::false_type{});
   run(fb, nq, std::true_type{});
@@ -421,6 +428,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   const int64_t BHN = (int64_t)p.B * p.H * N;
   const bool wave_has_rows = wrow < N;
   const int qrow = wrow + c;
+  const int W = p.window;  // causal sliding window (0: none)
 
   // Q_b^T and dO^T as B operands: lane n = query wrow + c, k = 16 t + 8 hh .. + 7
   bf16x8 qf[kD / 16], of[kDV / 16];
@@ -517,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
       float e = fmaf(s[r], sl2, -lse);
       if constexpr (MASK) {
         const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const bool vis = key < N && qrow < N && (!p.causal || key <= qrow);
+        const bool vis = key < N && qrow < N && (!p.causal || key <= qrow) && (W == 0 || qrow - key < W);
         e = vis ? e : -INFINITY;             // exp2(-inf) = 0: a select, not a branch
       }
       const float pr = __builtin_amdgcn_exp2f(e);
@@ -544,20 +552,24 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   const int ntiles = (kv_end + kT - 1) / kT;
   const int last_key = p.causal ? min(N, wrow + 32) : N;
   const int nt_wave = wave_has_rows ? min(ntiles, (last_key + kT - 1) / kT) : 0;
-  issue_tile(0, 0);
+  // first key tile the block's first row sees through the window, and this wave's own
+  const int kt_begin = W > 0 ? max(0, row0 - W + 1) / kT : 0;
+  const int kt_wave = W > 0 ? max(0, wrow - W + 1) / kT : 0;
+  issue_tile(kt_begin * kT, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // key tile kt sits in buffer kt & 1; two tiles per iteration keep the buffer index static
+  // key tile kt sits in buffer (kt - kt_begin) & 1; two tiles per iteration keep the buffer index
+  // static
   auto step = [&](int kt, auto buf_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
     if (kt + 1 < ntiles) issue_tile((kt + 1) * kT, BUF ^ 1);
-    if (kt < nt_wave) compute(kt, buf_tag, mask_tag);
+    if (kt >= kt_wave && kt < nt_wave) compute(kt, buf_tag, mask_tag);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   auto run = [&](int ka, int kb, auto mask_tag) __attribute__((always_inline)) {
     int kt = ka;
-    if (kt < kb && (kt & 1) != 0) step(kt++, std::integral_constant<int, 1>{}, mask_tag);
+    if (kt < kb && ((kt - kt_begin) & 1) != 0) step(kt++, std::integral_constant<int, 1>{}, mask_tag);
     for (; kt + 1 < kb; kt += 2) {
       step(kt, std::integral_constant<int, 0>{}, mask_tag);
       step(kt + 1, std::integral_constant<int, 1>{}, mask_tag);
@@ -566,9 +578,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   };
   // Key tiles [0, fe) need no mask for either wave: all their keys precede both waves' first row
   // (causal) and every row is inside N.  The diagonal and tail tiles run masked after them.
+  // With a window, the whole tiles also start only where the block's last row still sees the
+  // tile's first key: k0 >= row0 + 64 - W; the band's lower edge runs masked before them.
   const int fe = row0 + 64 <= N ? (p.causal ? row0 / kT : N / kT) : 0;
-  run(0, fe, std::false_type{});
-  run(fe, ntiles, std::true_type{});
+  const int fs = W > 0 ? min(max(kt_begin, (row0 + 64 - W + kT - 1 >= 0 ? (row0 + 64 - W + kT - 1) / kT : 0)), max(kt_begin, fe))
+                       : 0;
+  run(kt_begin, fs, std::true_type{});
+  run(fs, max(fs, fe), std::false_type{});
+  run(max(fs, fe), ntiles, std::true_type{});
   if (!wave_has_rows || qrow >= N) return;
   float* dqp = (br == 0 ? p.dq1 : p.dq2) + ((int64_t)bh * N + qrow) * kD;
 #pragma unroll

@@ -65,6 +65,7 @@ struct BwdParams {
   float* dv;             // [B, H, N, 2d]
   int32_t B, H, N;
   int32_t causal;
+  int32_t window;        // causal sliding window of the forward (0: none)
   int32_t n_row_blocks;  // 64-row query blocks (dQ) / 64-key blocks (dK, dV)
   float scale;           // 1 / sqrt(d)
   float scale_log2;      // log2(e) / sqrt(d)

@@ -141,7 +141,8 @@ da_status diffattn_fwd_v2_window(da_tensor q1, da_tensor q2, da_tensor k, da_ten
                                  void* stream);
 
 /*
- * Training: diffattn_fwd_v1_train is diffattn_fwd_v1 (bf16, d == 64, no window, norm on) that
+ * Training: diffattn_fwd_v1_train is diffattn_fwd_v1 (bf16, d == 64, norm on; window as in
+ * diffattn_fwd_v1_window, 0 for none, >= 1 only with causal = 1, DA_ERR_SHAPE otherwise) that
  * also writes a stash for the backward pass: each branch's normalised output O_b = A_b V and the
  * base-2 log-sum-exp of its scaled scores per row ([2, B, H, N, 2d] then [2, B, H, N] fp32,
  * followed by [2, B, H, N] fp32 that diffattn_bwd_v1 fills).  Size it with
@@ -150,8 +151,8 @@ da_status diffattn_fwd_v2_window(da_tensor q1, da_tensor q2, da_tensor k, da_ten
  * diffattn_bwd_v1 -- gradients of the V1 output (Ultralytics glossary "Differential
  * Transformer", section "Cómo funciona la atención diferencial"; ai-engineering.academy
  * "Atención Diferencial (V2)", section "La idea diferencial"): given dy = dL/dout [B, H, N, 2d]
- * (bf16, strided) and the same inputs, lambda, causal flag and eps as the training forward
- * whose stash is passed, it writes
+ * (bf16, strided) and the same inputs, lambda, causal flag, window and eps as the training
+ * forward whose stash is passed, it writes
  *   dq1, dq2, dk1, dk2 : fp32 contiguous [B, H, N, d];   dv : fp32 contiguous [B, H, N, 2d]
  *   dlam->dlq1 .. dlk2  : fp32 [H, dl] (required unless lam->lambda_override is set, in which
  *                         case lambda is an input with no vector gradients)
@@ -165,13 +166,14 @@ size_t diffattn_bwd_v1_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t 
 da_status diffattn_fwd_v1_train(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2,
                                 da_tensor v, da_tensor out, int32_t B, int32_t H, int32_t N,
                                 int32_t d, da_dtype dtype, const da_lambda* lam, int32_t causal,
-                                float eps, void* stash, size_t stash_bytes, void* stream);
+                                int32_t window, float eps, void* stash, size_t stash_bytes,
+                                void* stream);
 da_status diffattn_bwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2, da_tensor v,
                           da_tensor dy, float* dq1, float* dq2, float* dk1, float* dk2, float* dv,
                           int32_t B, int32_t H, int32_t N, int32_t d, da_dtype dtype,
                           const da_lambda* lam, const da_lambda_grad* dlam, int32_t causal,
-                          float eps, const void* stash, size_t stash_bytes, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          int32_t window, float eps, const void* stash, size_t stash_bytes,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace diffattn_decode needs for these sizes and split count

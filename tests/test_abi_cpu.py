@@ -242,8 +242,9 @@ def test_train_and_bwd_host_validation(da):
     stash = da.diffattn_v1_train_stash_bytes(B, H, N, 64)
     ws = da.diffattn_bwd_v1_workspace_bytes(B, H, N, 64)
 
-    def train(st=0x40000, nbytes=stash, d=64, dt=1, n=N, eps=1e-5):
-        return lib.diffattn_fwd_v1_train(*t6, B, H, n, d, dt, ctypes.byref(lam), 1, eps, st, nbytes, None)
+    def train(st=0x40000, nbytes=stash, d=64, dt=1, n=N, eps=1e-5, causal=1, window=0):
+        return lib.diffattn_fwd_v1_train(*t6, B, H, n, d, dt, ctypes.byref(lam), causal, window, eps,
+                                         st, nbytes, None)
 
     assert train(n=0) == 0                                   # empty: nothing enqueued
     assert train(n=-1) == 2
@@ -252,15 +253,17 @@ def test_train_and_bwd_host_validation(da):
     assert train(st=None) == 4
     assert train(nbytes=stash - 1) == 4
     assert train(st=0x40008) == 4                            # misaligned stash
+    assert train(window=-1) == 2
+    assert train(window=16, causal=0) == 2                   # the window is a causal one
 
     g = da_mod().DaLambdaGrad(0x50000, 0x50000, 0x50000, 0x50000)
     grads = [0x60000] * 5
 
     def bwd(gr=grads, lg=g, st=0x40000, sb=stash, w=0x70000, wb=ws, d=64, dt=1, n=N, eps=1e-5,
-            lm=lam):
+            lm=lam, causal=1, window=0):
         return lib.diffattn_bwd_v1(*t6, *gr, B, H, n, d, dt, ctypes.byref(lm),
-                                   ctypes.byref(lg) if lg is not None else None, 1, eps, st, sb,
-                                   w, wb, None)
+                                   ctypes.byref(lg) if lg is not None else None, causal, window,
+                                   eps, st, sb, w, wb, None)
 
     assert bwd(n=0) == 0
     assert bwd(n=-3) == 2
@@ -277,7 +280,9 @@ def test_train_and_bwd_host_validation(da):
     assert bwd(wb=ws - 1) == 4
     assert bwd(w=0x70008) == 4
     assert bwd(lm=_lam(layer=0)) == 2
+    assert bwd(window=-2) == 2
+    assert bwd(window=8, causal=0) == 2
     bad = list(t6)
     bad[5] = _t(ptr=0)
     assert lib.diffattn_bwd_v1(*bad, *grads, B, H, N, 64, 1, ctypes.byref(lam), ctypes.byref(g), 1,
-                               1e-5, 0x40000, stash, 0x70000, ws, None) == 1   # NULL dy
+                               0, 1e-5, 0x40000, stash, 0x70000, ws, None) == 1   # NULL dy

@@ -73,13 +73,14 @@ def _check_lambda_grads(g, ref):
         assert err <= 1.0, (k, err)
 
 
-def _run(da, t, layer, causal, dy):
+def _run(da, t, layer, causal, dy, window=0):
     import torch
 
     args = [dev(t[k]) for k in ("q1", "q2", "k1", "k2", "v")]
     lv = dev_lambda(t["lambda"][layer])
-    out, stash = da.diffattn_fwd_v1_train(*args, *lv, layer=layer, causal=causal)
-    g = da.diffattn_bwd_v1(*args, dev(dy), *lv, layer=layer, stash=stash, causal=causal)
+    out, stash = da.diffattn_fwd_v1_train(*args, *lv, layer=layer, causal=causal, window=window)
+    g = da.diffattn_bwd_v1(*args, dev(dy), *lv, layer=layer, stash=stash, causal=causal,
+                           window=window)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in g.items()}
 
@@ -209,3 +210,57 @@ def test_bwd_lambda_override_matches_vector_path(da):
     assert set(gb) == {"dq1", "dq2", "dk1", "dk2", "dv"}
     for k in gb:
         assert torch.equal(ga[k], gb[k]), k
+
+
+@pytest.mark.parametrize("B,H,N,window", [
+    (1, 1, 100, 1),      # each row sees only itself: dQ, dK vanish
+    (1, 2, 130, 33),     # window just past one tile, ragged tail
+    (2, 1, 257, 64),
+    (1, 2, 300, 100),
+    (1, 1, 200, 500),    # window covering every row: plain causal
+])
+def test_bwd_v1_window_against_oracle(da, B, H, N, window):
+    """Training with a causal sliding window (the forward's window, row i sees keys
+    i - window + 1 .. i): the training forward equals the window forward, and the gradients match
+    the oracle's backward through the same band."""
+    import torch
+
+    log(f"bwd v1 window B={B} H={H} N={N} window={window}")
+    layer = 7
+    t = wl.make_v1(B, H, N, 64, "bf16", seed=N + window, layers=(layer,))
+    dy = _dy((B, H, N, 128), seed=window)
+    out, g = _run(da, t, layer, True, dy, window=window)
+    fwd = da.diffattn_fwd_v1(*(dev(t[k]) for k in ("q1", "q2", "k1", "k2", "v")),
+                             *dev_lambda(t["lambda"][layer]), layer=layer, window=window)
+    torch.cuda.synchronize()
+    assert np.array_equal(out, fwd.float().cpu().numpy())
+    ref = oracle.diff_attn_v1_backward(*(f64(t[k]) for k in ("q1", "q2", "k1", "k2", "v")),
+                                       t["lambda"][layer], layer, f64(dy), True, 1e-5,
+                                       window=window)
+    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
+        if window == 1 and k != "dv":
+            assert np.max(np.abs(ref[k])) == 0.0
+            log(f"  {k} max |got| {np.max(np.abs(g[k])):.3e}")
+            assert np.max(np.abs(g[k])) <= 1e-5, k
+            continue
+        st = _slice_stats(g[k], ref[k])
+        log(f"  {k} {st}")
+        assert _ok(st), (k, st)
+    _check_lambda_grads(g, ref)
+
+
+def test_bwd_v1_window_workload_slice(da):
+    """The 1024-key window at the 4K shape, two heads, all gradients."""
+    layer, window = 12, 1024
+    t = wl.make_v1(1, 2, 4096, 64, "bf16", seed=1007, layers=(layer,))
+    dy = _dy((1, 2, 4096, 128), seed=78)
+    log("bwd v1 window 1024 N=4096 H=2")
+    _, g = _run(da, t, layer, True, dy, window=window)
+    ref = oracle.diff_attn_v1_backward(*(f64(t[k]) for k in ("q1", "q2", "k1", "k2", "v")),
+                                       t["lambda"][layer], layer, f64(dy), True, 1e-5,
+                                       window=window)
+    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
+        st = _slice_stats(g[k], ref[k])
+        log(f"  {k} {st}")
+        assert _ok(st), (k, st)
+    _check_lambda_grads(g, ref)
