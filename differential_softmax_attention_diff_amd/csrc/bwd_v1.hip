@@ -78,9 +78,12 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
     const float* o1 = p.stash_o + r * kDV + 8 * sub;
     const float* o2 = p.stash_o + (BHN + r) * kDV + 8 * sub;
     const bf16* dy = static_cast<const bf16*>(p.dy) + b * p.sdy.sb + h * p.sdy.sh + (int64_t)rc * p.sdy.sn + 8 * sub;
-    const f32x4 a1l = *reinterpret_cast<const f32x4*>(o1), a1h = *reinterpret_cast<const f32x4*>(o1 + 4);
-    const f32x4 a2l = *reinterpret_cast<const f32x4*>(o2), a2h = *reinterpret_cast<const f32x4*>(o2 + 4);
-    const u32x4 yw = load16(dy);
+    // read once: non-temporal
+    const f32x4 a1l = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o1));
+    const f32x4 a1h = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o1 + 4));
+    const f32x4 a2l = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o2));
+    const f32x4 a2h = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o2 + 4));
+    const u32x4 yw = load16_nt(dy);
     float a1[8], a2[8], y[8], x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -88,14 +88,14 @@ __global__ __launch_bounds__(kThreads) void decode_v1_partial_kernel(const Decod
       for (int br = 0; br < 2; ++br)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          kf[br][sb][t] = key < k_end ? load16(kb[br] + (int64_t)key * ksn[br] + 32 * t + 8 * grp)
+          kf[br][sb][t] = key < k_end ? load16_nt(kb[br] + (int64_t)key * ksn[br] + 32 * t + 8 * grp)
                                       : u32x4{0u, 0u, 0u, 0u};
     }
     u32x4 vf[16];
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
       const int key = blk + 64 * w + 4 * st + grp;
-      vf[st] = key < k_end ? load16(vbase + (int64_t)key * p.sv.sn + 8 * l16) : u32x4{0u, 0u, 0u, 0u};
+      vf[st] = key < k_end ? load16_nt(vbase + (int64_t)key * p.sv.sn + 8 * l16) : u32x4{0u, 0u, 0u, 0u};
     }
 
     // scores: D[m][n = key l16]; row m = 0 (lanes grp == 0, register 0) is the query's

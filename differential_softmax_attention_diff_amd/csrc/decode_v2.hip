@@ -126,14 +126,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
       const int key = blk + 64 * w + 16 * sb + l16;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        kf[sb][t] = key < k_end ? load16(kbase + row(key, blk, p.sk.sn) + 32 * t + 8 * grp)
+        kf[sb][t] = key < k_end ? load16_nt(kbase + row(key, blk, p.sk.sn) + 32 * t + 8 * grp)
                                 : u32x4{0u, 0u, 0u, 0u};
     }
     u32x4 vf[16];
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
       const int key = blk + 64 * w + 4 * st + grp;
-      vf[st] = key < k_end ? load16(vbase + row(key, blk, p.sv.sn) + 8 * l16) : u32x4{0u, 0u, 0u, 0u};
+      vf[st] = key < k_end ? load16_nt(vbase + row(key, blk, p.sv.sn) + 8 * l16) : u32x4{0u, 0u, 0u, 0u};
     }
 
     // scores: D[m = head 4*grp + r][n = key l16] for 16 keys per MFMA group

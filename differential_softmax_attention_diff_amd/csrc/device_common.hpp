@@ -55,6 +55,12 @@ __device__ __forceinline__ float head_lambda(const LambdaArgs& L, int idx, int l
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// 16-byte load marked non-temporal: for data streamed once (a decode step's KV cache), so that it
+// does not displace reused lines from the caches
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace da
