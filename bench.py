@@ -372,7 +372,7 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for "
               f"--gpus {a.gpus}); the per-GPU kernel is what one GPU shows.", file=sys.stderr)
         sys.exit(2)
 
