@@ -66,7 +66,7 @@ struct BwdParams {
   int32_t B, H, N;
   int32_t causal;
   int32_t window;        // causal sliding window of the forward (0: none)
-  int32_t n_row_blocks;  // 64-row query blocks (dQ) / 64-key blocks (dK, dV)
+  int32_t n_row_blocks;  // 64-key blocks of the dK/dV kernel
   float scale;           // 1 / sqrt(d)
   float scale_log2;      // log2(e) / sqrt(d)
   float eps;
