@@ -7,7 +7,8 @@ oracle baseline.  The same JSON line carries, under "secondary", each with its o
 V2 prefill (B=2, 32 query heads / 16 pairs over 8 KV heads, D=128, N=8192), the V2 decode step
 (B=64, 32 query / 8 KV heads, D=128, 32K-token cache), the same decode over a paged cache with
 ragged lengths, the V1 prefill under a 1024-key sliding window, the V1-layout decode step, and
-the V1 backward at the 4K training shape, causal and under the same window.
+the V1 backward at the 4K training shape, causal and under the same window, and a whole V1
+training step of the attention (training forward + backward).
 
 FLOP and byte conventions (per launch):
   V1 prefill  algorithmic flops  = B*H * 8*d * Np      (two QK^T products + one (A1-lambda A2)V)
@@ -19,7 +20,7 @@ FLOP and byte conventions (per launch):
 with Np = N(N+1)/2 causal query-key pairs (the window's visible pairs for the sliding window).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
-       [--only v1|v2|decode|decode_v1|swa|paged|bwd|bwd_swa]
+       [--only v1|v2|decode|decode_v1|swa|paged|bwd|bwd_swa|train]
        [--no-cpu-baseline] [--cpu-seconds S]
 """
 
@@ -318,6 +319,44 @@ def bench_bwd_v1(da, torch, steps, warmup, window=0):
     }
 
 
+def bench_train_step(da, torch, steps, warmup):
+    """One V1 training step of the attention at the 4K prefill shape: the training forward (output
+    plus the stash) followed by the backward for a seeded upstream gradient."""
+    cfg, t = wl.make("v1_prefill_4k")
+    layer = cfg["layers"][0]
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    args = [to_dev(t[k], torch) for k in ("q1", "q2", "k1", "k2", "v")]
+    lv = [torch.from_numpy(x).to("cuda") for x in t["lambda"][layer]]
+    rng = np.random.default_rng(77)
+    dy = to_dev(wl.f32_to_bf16_bits(rng.standard_normal((B, H, N, 2 * d), dtype=np.float32)), torch)
+    out = torch.empty((B, H, N, 2 * d), dtype=torch.bfloat16, device="cuda")
+    stash = torch.empty(da.diffattn_v1_train_stash_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(da.diffattn_bwd_v1_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    da.diffattn_fwd_v1_train(*args, *lv, layer=layer, out=out, stash=stash)
+    grads = da.diffattn_bwd_v1(*args, dy, *lv, layer=layer, stash=stash, workspace=ws)
+
+    def fn():
+        da.diffattn_fwd_v1_train(*args, *lv, layer=layer, out=out, stash=stash)
+        da.diffattn_bwd_v1(*args, dy, *lv, layer=layer, stash=stash, workspace=ws, grads=grads)
+    ms = time_launches(fn, steps, warmup, torch)
+    npairs = causal_pairs(N)
+    f_alg = B * H * (8 + 16) * d * npairs      # forward 8d, backward 16d per visible pair
+    f_exec = B * H * (12 + 40) * d * npairs
+    tf_alg = f_alg / (ms * 1e-3) / 1e12
+    tf_exec = f_exec / (ms * 1e-3) / 1e12
+    return {
+        "workload": "v1_train_step_4k", "ms": ms, "value": round(tf_alg, 2), "unit": "TFLOP/s",
+        "config": {"workload": "v1_train_step_4k", "B": B, "H": H, "N": N, "d": d, "dv": 2 * d,
+                   "causal": True, "layer": layer, "dtype": "bf16 in, fp32 gradients"},
+        "roofline": {"bound": "mfma", "achieved": round(tf_alg, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_alg / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "executed_mfma_tflops": round(tf_exec, 2),
+                     "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
+                     "kernel": "training forward (with stash) + backward"},
+    }
+
+
 # ------------------------------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the V1 workload)
 # ------------------------------------------------------------------------------------------------
@@ -364,7 +403,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)  # clocks settle after ~20-50 ms of load
-    ap.add_argument("--only", choices=["v1", "v2", "decode", "decode_v1", "swa", "paged", "bwd", "bwd_swa"],
+    ap.add_argument("--only", choices=["v1", "v2", "decode", "decode_v1", "swa", "paged", "bwd", "bwd_swa",
+                                       "train"],
                     default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -419,6 +459,10 @@ def main():
     if a.only in (None, "bwd"):
         print("[bench] v1 backward", file=sys.stderr, flush=True)
         secondary.append(bench_bwd_v1(da, torch, a.steps, a.warmup))
+        torch.cuda.empty_cache()
+    if a.only in (None, "train"):
+        print("[bench] v1 training step (forward + backward)", file=sys.stderr, flush=True)
+        secondary.append(bench_train_step(da, torch, a.steps, a.warmup))
         torch.cuda.empty_cache()
     if a.only in (None, "bwd_swa"):
         print("[bench] v1 backward, sliding window", file=sys.stderr, flush=True)
