@@ -16,7 +16,7 @@ FLOP and byte conventions (per launch):
   V2 prefill  algorithmic flops  = B*P * 6*D * Np,  executed = B*P * 8*D * Np
   decode      algorithmic bytes  = K and V cache + queries + output (every byte read once)
   V1 backward algorithmic flops  = B*H * 16*d * Np   (dO V^T, dV, and dQ_b, dK_b per branch)
-              executed MFMA flops = B*H * 40*d * Np  (scores and dO V^T formed in both kernels)
+              executed MFMA flops = B*H * 28*d * Np  (scores and dO V^T formed in both kernels)
 with Np = N(N+1)/2 causal query-key pairs (the window's visible pairs for the sliding window).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -300,9 +300,9 @@ def bench_bwd_v1(da, torch, steps, warmup, window=0):
     # gradient products: dP = dO V^T and dV = (A1 - lambda A2)^T dO (2d wide, once each), and
     # dQ_b = dS_b K_b, dK_b = dS_b^T Q_b per branch
     f_alg = B * H * 16 * d * npairs
-    # executed: dK/dV kernel S_b, X_b = dO V^T, dV_b, dK_b per branch (12d); dQ kernel S_b, X_b, dQ_b
-    # per branch (8d)
-    f_exec = B * H * 40 * d * npairs
+    # executed: dK/dV kernel S_1, S_2, X = dO V^T, dV, dK_1, dK_2 (16d); dQ kernel S_1, S_2, X,
+    # dQ_1, dQ_2 (12d)
+    f_exec = B * H * 28 * d * npairs
     tf_alg = f_alg / (ms * 1e-3) / 1e12
     tf_exec = f_exec / (ms * 1e-3) / 1e12
     return {
@@ -341,7 +341,7 @@ def bench_train_step(da, torch, steps, warmup):
     ms = time_launches(fn, steps, warmup, torch)
     npairs = causal_pairs(N)
     f_alg = B * H * (8 + 16) * d * npairs      # forward 8d, backward 16d per visible pair
-    f_exec = B * H * (12 + 40) * d * npairs
+    f_exec = B * H * (12 + 28) * d * npairs
     tf_alg = f_alg / (ms * 1e-3) / 1e12
     tf_exec = f_exec / (ms * 1e-3) / 1e12
     return {
