@@ -4,7 +4,8 @@ A step is one pass of the hot path over one batch of seeded synthetic input alre
 HBM.  The headline workload is the V1 prefill at a 4K context (B=4, H=16, N=4096, d=64, V width
 128, causal, bf16 in / fp32 accumulate, layer 12); its line carries the MFMA roofline and the CPU
 oracle baseline.  The same JSON line carries, under "secondary", each with its own roofline: the
-V2 prefill (B=2, 32 query heads / 16 pairs over 8 KV heads, D=128, N=8192), the V2 decode step
+V2 prefill (B=2, 32 query heads / 16 pairs over 8 KV heads, D=128, N=8192), the V1 prefill at a
+128K-token context (B=1, H=16, one layer of the 32-layer lambda sweep per launch), the V2 decode step
 (B=64, 32 query / 8 KV heads, D=128, 32K-token cache), the same decode over a paged cache with
 ragged lengths, the V1 prefill under a 1024-key sliding window, the V1-layout decode step, and
 the V1 backward at the 4K training shape, causal and under the same window, and a whole V1
@@ -20,7 +21,7 @@ FLOP and byte conventions (per launch):
 with Np = N(N+1)/2 causal query-key pairs (the window's visible pairs for the sliding window).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
-       [--only v1|v2|decode|decode_v1|swa|paged|bwd|bwd_swa|train]
+       [--only v1|v2|long|decode|decode_v1|swa|paged|bwd|bwd_swa|train]
        [--no-cpu-baseline] [--cpu-seconds S]
 """
 
@@ -153,6 +154,45 @@ def bench_v2(da, torch, steps, warmup):
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
                      "kernel": "prefill_kernel<128,true,true>"},
+    }
+
+
+def bench_long(da, torch, steps, warmup):
+    """V1 prefill at a 128K-token context with planted needles; launch i uses layer 1 + i % 32, so
+    a full set of timed launches sweeps the lambda schedule (one layer per launch)."""
+    cfg, t = wl.make("v1_long_128k")
+    layers = cfg["layers"]
+    B, H, N, d = cfg["B"], cfg["H"], cfg["N"], cfg["d"]
+    args = [to_dev(t[k], torch) for k in ("q1", "q2", "k1", "k2", "v")]
+    lvs = [[torch.from_numpy(x).to("cuda") for x in t["lambda"][l]] for l in layers]
+    del t
+    out = torch.empty((B, H, N, 2 * d), dtype=torch.bfloat16, device="cuda")
+    count = [0]
+
+    def fn():
+        i = count[0] % len(layers)
+        count[0] += 1
+        da.diffattn_fwd_v1(*args, *lvs[i], layer=layers[i], out=out)
+
+    # about 0.1 s per launch: a few warm-up launches settle the clock; the timed launches cover
+    # every layer of the sweep once
+    ms = time_launches(fn, max(steps, len(layers)) // len(layers) * len(layers), min(warmup, 8), torch)
+    npairs = causal_pairs(N)
+    f_alg = B * H * 8 * d * npairs
+    f_exec = B * H * 12 * d * npairs
+    tf_alg = f_alg / (ms * 1e-3) / 1e12
+    tf_exec = f_exec / (ms * 1e-3) / 1e12
+    return {
+        "workload": "v1_long_128k", "ms": ms, "value": round(tf_alg, 2), "unit": "TFLOP/s",
+        "config": {"workload": "v1_long_128k", "B": B, "H": H, "N": N, "d": d, "dv": 2 * d,
+                   "causal": True, "layers": f"{layers[0]}..{layers[-1]} (one per launch)",
+                   "needles_per_head": cfg["needles"], "dtype": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(tf_alg, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf_alg / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("v1_long_128k", "prefill"),
+                     "executed_mfma_tflops": round(tf_exec, 2),
+                     "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
+                     "kernel": "prefill_kernel<64,false,false>"},
     }
 
 
@@ -403,8 +443,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)  # clocks settle after ~20-50 ms of load
-    ap.add_argument("--only", choices=["v1", "v2", "decode", "decode_v1", "swa", "paged", "bwd", "bwd_swa",
-                                       "train"],
+    ap.add_argument("--only", choices=["v1", "v2", "long", "decode", "decode_v1", "swa", "paged", "bwd",
+                                       "bwd_swa", "train"],
                     default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -439,6 +479,10 @@ def main():
     if a.only in (None, "v2"):
         print("[bench] v2 prefill", file=sys.stderr, flush=True)
         secondary.append(bench_v2(da, torch, a.steps, a.warmup))
+        torch.cuda.empty_cache()
+    if a.only in (None, "long"):
+        print("[bench] v1 prefill, 128K context", file=sys.stderr, flush=True)
+        secondary.append(bench_long(da, torch, a.steps, a.warmup))
         torch.cuda.empty_cache()
     if a.only in (None, "decode"):
         print("[bench] v2 decode", file=sys.stderr, flush=True)
