@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
   diffattn_fwd_v1(q1, q2, k1, k2, v, lq1, lk1, lq2, lk2, layer, ...)   V1 prefill
   diffattn_fwd_v2(q1, q2, k, v, lq1, lk1, lq2, lk2, layer, ...)        V2 prefill (GQA pairs)
   (both take window=W for the causal sliding window: diffattn_fwd_v1_window / _v2_window)
+  diffattn_fwd_v2_workspace_bytes(B, Hkv, N, D)
   diffattn_decode(q1, q2, kcache, vcache, lq1, lk1, lq2, lk2, layer, ...)  V2 decode step
   diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits=0)
   diffattn_decode_paged(q1, q2, k_pages, v_pages, block_table, seq_lens, lq1, ...)  V2 decode,
@@ -32,7 +33,8 @@ __all__ = [
     "diffattn_fwd_v1", "diffattn_fwd_v2", "diffattn_decode", "diffattn_decode_v1",
     "diffattn_decode_paged", "diffattn_fwd_v1_train", "diffattn_bwd_v1",
     "diffattn_v1_train_stash_bytes", "diffattn_bwd_v1_workspace_bytes",
-    "diffattn_decode_workspace_bytes", "diffattn_decode_v1_workspace_bytes", "diffattn_lambda_init",
+    "diffattn_fwd_v2_workspace_bytes", "diffattn_decode_workspace_bytes",
+    "diffattn_decode_v1_workspace_bytes", "diffattn_lambda_init",
     "diffattn_status_string", "diffattn_version",
 ]
 
@@ -85,11 +87,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     i32, u32, f32, vp, sz = ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
     lib.diffattn_fwd_v1.argtypes = [T, T, T, T, T, T, i32, i32, i32, i32, i32, L, i32, f32, u32, vp]
     lib.diffattn_fwd_v1.restype = i32
-    lib.diffattn_fwd_v2.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp]
+    lib.diffattn_fwd_v2_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.diffattn_fwd_v2_workspace_bytes.restype = sz
+    lib.diffattn_fwd_v2.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp, sz, vp]
     lib.diffattn_fwd_v2.restype = i32
     lib.diffattn_fwd_v1_window.argtypes = [T, T, T, T, T, T, i32, i32, i32, i32, i32, L, i32, f32, u32, vp]
     lib.diffattn_fwd_v1_window.restype = i32
-    lib.diffattn_fwd_v2_window.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp]
+    lib.diffattn_fwd_v2_window.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp, sz, vp]
     lib.diffattn_fwd_v2_window.restype = i32
     lib.diffattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.diffattn_decode_workspace_bytes.restype = sz
@@ -134,6 +138,10 @@ def diffattn_version() -> str:
 
 def diffattn_lambda_init(layer: int) -> float:
     return float(load_library().diffattn_lambda_init(int(layer)))
+
+
+def diffattn_fwd_v2_workspace_bytes(B, Hkv, N, D) -> int:
+    return int(load_library().diffattn_fwd_v2_workspace_bytes(B, Hkv, N, D))
 
 
 def diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits: int = 0) -> int:
@@ -256,10 +264,11 @@ def diffattn_fwd_v1(q1, q2, k1, k2, v, lq1=None, lk1=None, lq2=None, lk2=None, l
 
 def diffattn_fwd_v2(q1, q2, k, v, lq1=None, lk1=None, lq2=None, lk2=None, layer=1, *,
                     out=None, causal=True, window=0, lambda_override=None, lambda_out=None,
-                    stream=None):
+                    workspace=None, stream=None):
     """V2 differential attention; q1, q2 [B, P, N, D] (query heads 2p and 2p+1), k, v [B, Hkv, N, D]
     -> out [B, P, N, D].  Pair p reads KV head p * Hkv // P.  ``window`` > 0 selects the causal
-    sliding window (``diffattn_fwd_v2_window``)."""
+    sliding window (``diffattn_fwd_v2_window``).  ``workspace``: a device uint8 tensor of at least
+    ``diffattn_fwd_v2_workspace_bytes(B, Hkv, N, D)`` bytes (allocated here when None)."""
     torch = _torch()
     B, P, N, D = q1.shape
     Hkv = k.shape[1]
@@ -273,17 +282,23 @@ def diffattn_fwd_v2(q1, q2, k, v, lq1=None, lk1=None, lq2=None, lk2=None, layer=
              _desc(k, "k", (B, Hkv, N, D)), _desc(v, "v", (B, Hkv, N, D)),
              _desc(out, "out", (B, P, N, D))]
     lam = _lambda(lq1, lk1, lq2, lk2, layer, P, lambda_override, lambda_out, q1.device)
+    if window and not causal:
+        raise ValueError("the sliding window is a causal one")
+    if workspace is None:
+        workspace = torch.empty(max(16, diffattn_fwd_v2_workspace_bytes(B, Hkv, N, D)), dtype=torch.uint8,
+                                device=q1.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with torch.cuda.device(q1.device):
         st = _stream(q1.device, stream)
         if window:
-            if not causal:
-                raise ValueError("the sliding window is a causal one")
             _check(load_library().diffattn_fwd_v2_window(*descs, B, P, Hkv, N, D, dt,
-                                                         ctypes.byref(lam), int(window), st),
+                                                         ctypes.byref(lam), int(window), ws, ws_bytes, st),
                    "diffattn_fwd_v2_window")
         else:
             _check(load_library().diffattn_fwd_v2(*descs, B, P, Hkv, N, D, dt, ctypes.byref(lam),
-                                                  1 if causal else 0, st), "diffattn_fwd_v2")
+                                                  1 if causal else 0, ws, ws_bytes, st), "diffattn_fwd_v2")
     return out
 
 

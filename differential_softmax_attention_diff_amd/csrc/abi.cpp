@@ -148,9 +148,17 @@ da_status fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2, da_tens
   return hip_status(da::launch_v1_bf16(p, st));
 }
 
+// Bytes of the V2 prefill workspace: the fp16 copy of V, then one flag byte per 16-key x
+// 64-channel region (4 per 32-key tile), the flags starting on a 256-byte boundary.
+int64_t v2_values_bytes(int32_t B, int32_t Hkv, int32_t N) { return ((int64_t)B * Hkv * N * 128 * 2 + 255) / 256 * 256; }
+int64_t v2_workspace_bytes(int32_t B, int32_t Hkv, int32_t N) {
+  return v2_values_bytes(B, Hkv, N) + (int64_t)B * Hkv * ((N + 31) / 32) * 4;
+}
+
 da_status fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor out, int32_t B,
                  int32_t P, int32_t Hkv, int32_t N, int32_t D, da_dtype dtype,
-                 const da_lambda* lam, int32_t causal, int32_t window, void* stream) {
+                 const da_lambda* lam, int32_t causal, int32_t window, void* workspace,
+                 size_t workspace_bytes, void* stream) {
   if (B < 0 || P < 0 || Hkv < 0 || N < 0 || window < 0) return DA_ERR_SHAPE;
   if (window > 0 && !causal) return DA_ERR_SHAPE;
   if (B == 0 || P == 0 || N == 0) return DA_OK;
@@ -159,6 +167,7 @@ da_status fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor
   if (D != 128) return D <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
   if (P % Hkv != 0) return DA_ERR_SHAPE;
   if ((int64_t)B * P > (int64_t)INT32_MAX || (N + 63) / 64 > kMaxGridY) return DA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv > kMaxGridY) return DA_ERR_UNSUPPORTED;
   for (const da_tensor* t : {&q1, &q2, &k, &v, &out}) {
     const da_status s = check_tensor(*t, 2);
     if (s != DA_OK) return s;
@@ -167,6 +176,9 @@ da_status fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor
   if (s != DA_OK) return s;
   for (const da_tensor* t : {&q1, &q2, &k, &v})
     if (!rows_fit_32bit(*t, N, 2)) return DA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < (size_t)v2_workspace_bytes(B, Hkv, N))
+    return DA_ERR_WORKSPACE;
 
   da::PrefillParams p{};
   p.q1 = q1.ptr; p.q2 = q2.ptr; p.k1 = k.ptr; p.k2 = k.ptr; p.v = v.ptr; p.out = out.ptr;
@@ -181,6 +193,8 @@ da_status fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor
   p.eps = 0.f;
   p.out_scale = 1.f;
   p.lam = lambda_args(lam);
+  p.vh = workspace;
+  p.vflags = static_cast<uint8_t*>(workspace) + v2_values_bytes(B, Hkv, N);
   return hip_status(da::launch_v2_bf16(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -203,18 +217,26 @@ da_status diffattn_fwd_v1_window(da_tensor q1, da_tensor q2, da_tensor k1, da_te
   return fwd_v1(q1, q2, k1, k2, v, out, B, H, N, d, dtype, lam, 1, window, eps, flags, stream);
 }
 
+size_t diffattn_fwd_v2_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t D) {
+  if (B <= 0 || Hkv <= 0 || N <= 0 || D != 128) return 0;
+  return (size_t)v2_workspace_bytes(B, Hkv, N);
+}
+
 da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor out,
                           int32_t B, int32_t P, int32_t Hkv, int32_t N, int32_t D,
-                          da_dtype dtype, const da_lambda* lam, int32_t causal, void* stream) {
-  return fwd_v2(q1, q2, k, v, out, B, P, Hkv, N, D, dtype, lam, causal, 0, stream);
+                          da_dtype dtype, const da_lambda* lam, int32_t causal, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return fwd_v2(q1, q2, k, v, out, B, P, Hkv, N, D, dtype, lam, causal, 0, workspace,
+                workspace_bytes, stream);
 }
 
 da_status diffattn_fwd_v2_window(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v,
                                  da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t N,
                                  int32_t D, da_dtype dtype, const da_lambda* lam, int32_t window,
-                                 void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   if (window < 1) return DA_ERR_SHAPE;
-  return fwd_v2(q1, q2, k, v, out, B, P, Hkv, N, D, dtype, lam, 1, window, stream);
+  return fwd_v2(q1, q2, k, v, out, B, P, Hkv, N, D, dtype, lam, 1, window, workspace,
+                workspace_bytes, stream);
 }
 
 size_t diffattn_decode_workspace_bytes(int32_t B, int32_t P, int32_t Hkv, int32_t L, int32_t D,

@@ -47,6 +47,12 @@ struct PrefillParams {
   // scaled scores, for the backward pass (null: not written)
   float* stash_o;        // [2, B, H, N, 2d]
   float* stash_lse;      // [2, B, H, N]
+  // V2: V rewritten once per call as fp16, contiguous [B, Hkv, N, 128], per region of 16 keys x
+  // 64 channels (kept as bf16 where the region holds a value beyond the fp16 range), and one flag
+  // byte per region, [B, Hkv, ceil(N / 32), 4]: byte 2u + c of a 32-key tile is its key half u,
+  // channel half c (1: bf16)
+  void* vh;
+  uint8_t* vflags;
 };
 
 // V1 backward.  Inputs bf16 (strided); gradients fp32, contiguous.

@@ -37,9 +37,10 @@
 //    are issued heaviest first; all row blocks of a head (V1) or all pairs of a KV head (V2)
 //    land on one XCD.
 //  * F16PV (V2): P.V runs on the fp16 MFMA (P and V rounded to fp16, 11 significant bits instead
-//    of bf16's 8).  Each wave stages one 16-key x 64-channel region of the next V tile through
-//    registers and stores it as fp16, or as bf16 when the region holds a value beyond the fp16
-//    range; a per-region flag in LDS sends the wave to a bf16 P.V loop from that tile on.
+//    of bf16's 8).  v2_values_kernel rewrites V once per call as fp16, region by region (16 keys
+//    x 64 channels), keeping bf16 where a region holds a value beyond the fp16 range, with one
+//    flag byte per region; the prefill streams those tiles like any other and reads a tile's four
+//    flags as one word, and a set flag sends the wave to a bf16 P.V loop from that tile on.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -86,9 +87,8 @@ void prefill_kernel(const PrefillParams p) {
   using C = SCfg<DQK, V2, NS>;
   constexpr int BM = 64;
   __shared__ __attribute__((aligned(1024))) bf16 smem[C::SMEM];
-  __shared__ int vflag[NS][4];
   static_assert(C::SMEM * 2 >= 2 * 64 * 64 * 4, "epilogue exchange must fit the tile buffers");
-  static_assert(!F16PV || NS == 2, "F16PV converts the next tile's V in the same iteration");
+  static_assert(!F16PV || NS == 2, "F16PV keeps the flags of one tile ahead");
   constexpr uint32_t kKB = C::KBUF * 2, kVB = C::VBUF * 2;  // bytes per K / V buffer
 
   const int tid = threadIdx.x;
@@ -148,18 +148,24 @@ void prefill_kernel(const PrefillParams p) {
   const int t0_wave = p.window > 0 ? max(t_begin, max(0, wrow - p.window + 1) / kSBN) : 0;
 
   const uint32_t k1_row = (uint32_t)(p.sk1.sn * 2), k2_row = (uint32_t)(p.sk2.sn * 2);
-  const uint32_t v_row = (uint32_t)(p.sv.sn * 2);
+  // F16PV: V comes from the fp16 copy, contiguous rows of 256 bytes
+  const int64_t vhead = (int64_t)b * p.Hkv + kvh;
+  const uint32_t v_row = F16PV ? (uint32_t)(kDV * 2) : (uint32_t)(p.sv.sn * 2);
   const char* k1_base = static_cast<const char*>(p.k1) + 2 * (b * p.sk1.sb + kvh * p.sk1.sh);
   const char* k2_base = static_cast<const char*>(p.k2) + 2 * (b * p.sk2.sb + kvh * p.sk2.sh);
-  const char* v_base = static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + kvh * p.sv.sh);
+  const char* v_base = F16PV ? static_cast<const char*>(p.vh) + vhead * N * (kDV * 2)
+                             : static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + kvh * p.sv.sh);
+  // F16PV: the flag word of each 32-key tile of this KV head
+  const uint32_t* vflag_words = F16PV ? reinterpret_cast<const uint32_t*>(p.vflags) + vhead * ((N + kSBN - 1) / kSBN)
+                                      : nullptr;
 
   // ---- tile loads.  Wave w issues the 1 KB DMA loads j = w + 4i of a K buffer (K1 then K2 in
-  // V1) and of a V buffer (unless V is staged through registers).  Lane offsets are relative to
-  // the tile's first row, which moves into the scalar buffer base.
-  constexpr int KPW = C::K_LOADS / 4;              // per wave per K tensor
-  constexpr int VPW = F16PV ? 0 : C::V_LOADS / 4;  // per wave, V
+  // V1) and of a V buffer.  Lane offsets are relative to the tile's first row, which moves into
+  // the scalar buffer base.
+  constexpr int KPW = C::K_LOADS / 4;  // per wave per K tensor
+  constexpr int VPW = C::V_LOADS / 4;  // per wave, V
   uint32_t k_lane[C::NK][KPW];
-  uint32_t v_lane[VPW > 0 ? VPW : 1];
+  uint32_t v_lane[VPW];
 #pragma unroll
   for (int nk = 0; nk < C::NK; ++nk)
 #pragma unroll
@@ -177,16 +183,11 @@ void prefill_kernel(const PrefillParams p) {
     const int lcol = ((((slot >> 1) ^ (2 * (row & 3)))) << 4) + ((slot & 1) << 3);
     v_lane[i] = (uint32_t)row * v_row + lcol * 2;
   }
-  // F16PV staging region of this wave: rows 16 (w >> 1) + q / 8, channels 64 (w & 1) + 8 (q % 8)
-  // for q = lane + 64 s.
-  int vs_row[2], vs_col[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int q = lane + 64 * s;
-    vs_row[s] = 16 * (w >> 1) + (q >> 3);
-    vs_col[s] = 64 * (w & 1) + 8 * (q & 7);
-  }
-  u32x4 vreg[2];
+  // F16PV: flag word of the tile being computed and of the tile being loaded
+  uint32_t fw_cur = 0, fw_next = 0;
+  auto load_flags = [&](int i) -> uint32_t {
+    return F16PV ? __builtin_amdgcn_readfirstlane(vflag_words[i]) : 0u;
+  };
 
   auto issue_k = [&](int kt, int buf) {
     bf16* kb = smem + buf * C::KBUF;
@@ -203,36 +204,9 @@ void prefill_kernel(const PrefillParams p) {
   auto issue_v = [&](int kt, int buf) {
     const int rows_left = N - kt;
     const __amdgpu_buffer_rsrc_t rvt = make_rsrc(v_base + (size_t)kt * v_row, (uint32_t)rows_left * v_row);
-    if constexpr (!F16PV) {
-      bf16* vb = smem + NS * C::KBUF + buf * C::VBUF;
-#pragma unroll
-      for (int i = 0; i < VPW; ++i) dma16(rvt, vb + 512 * (w + 4 * i), v_lane[i]);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) vreg[s] = bload16(rvt, (uint32_t)vs_row[s] * v_row + vs_col[s] * 2);
-    }
-  };
-  // F16PV: convert the staged region (unless it holds a value fp16 cannot represent), store it,
-  // and publish the region's format
-  auto finish_v = [&](int buf) {
     bf16* vb = smem + NS * C::KBUF + buf * C::VBUF;
-    float mx = 0.f;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(vreg[s][m])), fabsf(bf16_hi(vreg[s][m]))));
-    const bool big = __any(mx > kF16Max);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4 x = vreg[s];
-      if (!big) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) x[m] = pack_h2(bf16_lo(vreg[s][m]), bf16_hi(vreg[s][m]));
-      }
-      store16(vb + v_off(vs_row[s], vs_col[s]), x);
-    }
-    if (lane == 0) vflag[buf][w] = big ? 1 : 0;
+    for (int i = 0; i < VPW; ++i) dma16(rvt, vb + 512 * (w + 4 * i), v_lane[i]);
   };
   auto issue_tile = [&](int i) {
     issue_k(i * kSBN, i % NS);
@@ -356,7 +330,6 @@ void prefill_kernel(const PrefillParams p) {
     lrun += tl;
 
     // O^T += V^T P^T, 16 keys per MFMA
-    const int vbuf = buf;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -372,7 +345,7 @@ void prefill_kernel(const PrefillParams p) {
           // bf16 P.V; on the F16PV slow path the fp16 regions are widened back to bf16 (exact for
           // every value fp16 holds with 8 or more significant bits)
           if constexpr (kSlow) {
-            if (!vflag[vbuf][2 * u + (db >> 1)]) a4 = f16x8_to_bf16x8(a4);
+            if (((fw_cur >> (8 * (2 * u + (db >> 1)))) & 0xffu) == 0u) a4 = f16x8_to_bf16x8(a4);
           }
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
                                                            __builtin_bit_cast(bf16x8, pp), acc[db], 0, 0, 0);
@@ -387,10 +360,7 @@ void prefill_kernel(const PrefillParams p) {
   // the loop that carries the accumulators has no path around them.  F16PV: from the first tile
   // with a bf16 region on, a wave stays on the bf16 path, in a loop of its own so that the
   // accumulators never merge from two paths inside one loop.
-  auto tile_big = [&](int i) {
-    const int vb = i % NS;
-    return F16PV && (vflag[vb][0] | vflag[vb][1] | vflag[vb][2] | vflag[vb][3]) != 0;
-  };
+  auto tile_big = [&](int) { return F16PV && fw_cur != 0u; };
   // Iteration i loads tile i + NS - 1 into the buffer tile i - 1 used, computes tile i, and waits
   // until tile i + 1 has landed: with NS > 2 the loads of the tiles after it stay in flight
   // (vmcnt counts this wave's outstanding buffer loads, which complete in order).
@@ -407,20 +377,18 @@ void prefill_kernel(const PrefillParams p) {
   auto step = [&](int i, auto slow_tag) {
     const int ahead = i + NS - 1;
     const bool more = ahead < ntiles;
-    if (more) issue_tile(ahead);
-    compute_tile(i, slow_tag);
-    if constexpr (F16PV) {
-      if (more) finish_v(ahead % NS);
+    if (more) {
+      issue_tile(ahead);
+      fw_next = load_flags(ahead);
     }
+    compute_tile(i, slow_tag);
     wait_next(i);
     __syncthreads();
+    fw_cur = fw_next;
   };
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) {
-    if (t_begin + i < ntiles) {
-      issue_tile(t_begin + i);
-      if constexpr (F16PV) finish_v((t_begin + i) % NS);
-    }
+    if (t_begin + i < ntiles) issue_tile(t_begin + i);
   }
   if constexpr (NS == 2 || F16PV) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -429,15 +397,17 @@ void prefill_kernel(const PrefillParams p) {
     else __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
+  if (t_begin < ntiles) fw_cur = load_flags(t_begin);
   // tiles before this wave's window only need its share of the loads and the barriers
   auto help = [&](int i) {
     const int ahead = i + NS - 1;
     if (ahead < ntiles) {
       issue_tile(ahead);
-      if constexpr (F16PV) finish_v(ahead % NS);
+      fw_next = load_flags(ahead);
     }
     wait_next(i);
     __syncthreads();
+    fw_cur = fw_next;
   };
   int it = t_begin;
   for (; it < t0_wave; ++it) help(it);
@@ -511,6 +481,48 @@ void prefill_kernel(const PrefillParams p) {
     }
 }
 
+// V2 values for the fp16 P.V: one workgroup per 32-key tile of a KV head, one wave per region
+// of 16 keys x 64 channels (rows 16 (w >> 1) + q / 8, channels 64 (w & 1) + 8 (q % 8) for
+// q = lane + 64 s).  A region is written as fp16 unless it holds a value beyond the fp16 range
+// (then as its bf16 bits), and its flag byte says which.  Rows past N are neither read (the
+// buffer range check returns zeros) nor written.
+__global__ __launch_bounds__(kThreads) void v2_values_kernel(const PrefillParams p) {
+  const int tile = blockIdx.x;
+  const int bh = blockIdx.y;  // b * Hkv + KV head
+  const int b = bh / p.Hkv, kvh = bh % p.Hkv;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int N = p.N;
+  const int kt = tile * kSBN;
+  const uint32_t v_row = (uint32_t)(p.sv.sn * 2);
+  const char* vsrc = static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + kvh * p.sv.sh);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vsrc + (size_t)kt * v_row, (uint32_t)(N - kt) * v_row);
+  u32x4 x[2];
+  int row[2], col[2];
+  float mx = 0.f;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int q = lane + 64 * s;
+    row[s] = 16 * (w >> 1) + (q >> 3);
+    col[s] = 64 * (w & 1) + 8 * (q & 7);
+    x[s] = bload16(rv, (uint32_t)row[s] * v_row + col[s] * 2);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(x[s][m])), fabsf(bf16_hi(x[s][m]))));
+  }
+  const bool big = __any(mx > kF16Max);
+  bf16* dst = static_cast<bf16*>(p.vh) + (int64_t)bh * N * kDV;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    u32x4 y = x[s];
+    if (!big) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) y[m] = pack_h2(bf16_lo(x[s][m]), bf16_hi(x[s][m]));
+    }
+    if (kt + row[s] < N) store16(dst + (int64_t)(kt + row[s]) * kDV + col[s], y);
+  }
+  if (lane == 0) p.vflags[((int64_t)bh * gridDim.x + tile) * 4 + w] = big ? 1 : 0;
+}
+
 }  // namespace
 
 hipError_t launch_v1_bf16(const PrefillParams& p, hipStream_t stream) {
@@ -525,6 +537,7 @@ hipError_t launch_v2_bf16(const PrefillParams& p, hipStream_t stream) {
   PrefillParams q = p;
   q.pairs_per_kv = p.heads / p.Hkv;
   q.n_row_blocks = (p.N + 63) / 64;
+  hipLaunchKernelGGL(v2_values_kernel, dim3((p.N + kSBN - 1) / kSBN, p.B * p.Hkv), dim3(kThreads), 0, stream, q);
   const dim3 grid(p.B * p.heads, q.n_row_blocks);
   hipLaunchKernelGGL((prefill_kernel<128, true, true, 2>), grid, dim3(kThreads), 0, stream, q);
   return hipGetLastError();

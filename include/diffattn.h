@@ -104,6 +104,14 @@ da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2
                           uint32_t flags, void* stream);
 
 /*
+ * Bytes of device workspace diffattn_fwd_v2 and diffattn_fwd_v2_window need: the value tensor
+ * rewritten once per call in the 16-bit format the P.V products use (B * Hkv * N * 256 bytes,
+ * rounded up to 256) plus one byte per 16-key x 64-channel region (B * Hkv * ceil(N / 32) * 4).
+ * Returns 0 for unsupported sizes (D != 128, non-positive dimensions).
+ */
+size_t diffattn_fwd_v2_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t D);
+
+/*
  * diffattn_fwd_v2 -- V2 layout (ai-engineering.academy "Atención Diferencial (V2)", sections
  * "V1 vs V2: la diferencia" and "Ejercicios" 5): 2P query heads of full width D paired as
  * (2p, 2p+1) over Hkv shared KV heads; pair p reads KV head p * Hkv / P.
@@ -113,20 +121,25 @@ da_status diffattn_fwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2
  *   k, v : [B, Hkv, N, D]                out : [B, P, N, D]       lambda vectors: [P, dl]
  *   out[b,p,i,:] = softmax(q1 k^T / sqrt(D)) v - lambda_p softmax(q2 k^T / sqrt(D)) v
  *   (no normalisation, no scale).
+ *   workspace : device buffer of at least diffattn_fwd_v2_workspace_bytes(B, Hkv, N, D) bytes,
+ *               16-byte aligned, owned by the caller; its contents on entry do not matter and are
+ *               clobbered (DA_ERR_WORKSPACE if NULL, misaligned or too small).  Calls that share
+ *               one workspace must be ordered (one stream).
  *
- * Supported: D == 128, dtype DA_BF16, P % Hkv == 0.
+ * Supported: D == 128, dtype DA_BF16, P % Hkv == 0, B * Hkv <= 65535.
  */
 da_status diffattn_fwd_v2(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v, da_tensor out,
                           int32_t B, int32_t P, int32_t Hkv, int32_t N, int32_t D,
-                          da_dtype dtype, const da_lambda* lam, int32_t causal, void* stream);
+                          da_dtype dtype, const da_lambda* lam, int32_t causal, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * diffattn_fwd_v1_window, diffattn_fwd_v2_window -- the same two layouts restricted to a causal
  * sliding window, for the window layers of hybrid DIFF / sliding-window stacks
  * (ai-engineering.academy "Atención Diferencial (V2)", section "Úselo").  Query row i sees keys
  * i - window + 1 .. i (its last `window` positions, itself included); window >= N is plain
- * causal.  Arguments, layouts and results are those of diffattn_fwd_v1 / diffattn_fwd_v2 with
- * causal = 1, and:
+ * causal.  Arguments, layouts and results (and the V2 workspace) are those of diffattn_fwd_v1 /
+ * diffattn_fwd_v2 with causal = 1, and:
  *   window : >= 1 (DA_ERR_SHAPE otherwise).
  * A decode step over a window needs no entry point of its own: pass the last `window` cache
  * rows (a strided view) to diffattn_decode / diffattn_decode_v1.
@@ -138,7 +151,7 @@ da_status diffattn_fwd_v1_window(da_tensor q1, da_tensor q2, da_tensor k1, da_te
 da_status diffattn_fwd_v2_window(da_tensor q1, da_tensor q2, da_tensor k, da_tensor v,
                                  da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t N,
                                  int32_t D, da_dtype dtype, const da_lambda* lam, int32_t window,
-                                 void* stream);
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Training: diffattn_fwd_v1_train is diffattn_fwd_v1 (bf16, d == 64, norm on; window as in

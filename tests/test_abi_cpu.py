@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_header_symbols_exported(da):
     names = _declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -100,12 +100,18 @@ def test_v2_and_decode_host_validation(da):
     lib = da.load_library()
     t5 = [_t() for _ in range(5)]
     lam = _lam(dl=128)
-    assert lib.diffattn_fwd_v2(*t5, 1, 3, 2, 8, 128, 1, ctypes.byref(lam), 1, None) == 2  # P % Hkv
-    assert lib.diffattn_fwd_v2(*t5, 1, 4, 2, 8, 64, 1, ctypes.byref(lam), 1, None) == 3   # D
-    assert lib.diffattn_fwd_v2(*t5, 1, 4, 2, 8, 128, 0, ctypes.byref(lam), 1, None) == 3  # fp32
-    assert lib.diffattn_fwd_v2(*t5, 1, 4, 0, 8, 128, 1, ctypes.byref(lam), 1, None) == 2
-    assert lib.diffattn_fwd_v2(*t5, 0, 4, 2, 8, 128, 1, ctypes.byref(lam), 1, None) == 0
-    assert lib.diffattn_fwd_v2(*t5, 1, 1 << 16, 2, 1 << 22, 128, 1, ctypes.byref(lam), 1, None) == 3  # grid
+    v2ws = da.diffattn_fwd_v2_workspace_bytes(1, 2, 8, 128)
+    v2 = lambda B, P, Hkv, N, D, dt, ws=0x40000, nbytes=v2ws: lib.diffattn_fwd_v2(
+        *t5, B, P, Hkv, N, D, dt, ctypes.byref(lam), 1, ws, nbytes, None)
+    assert v2(1, 3, 2, 8, 128, 1) == 2  # P % Hkv
+    assert v2(1, 4, 2, 8, 64, 1) == 3   # D
+    assert v2(1, 4, 2, 8, 128, 0) == 3  # fp32
+    assert v2(1, 4, 0, 8, 128, 1) == 2
+    assert v2(0, 4, 2, 8, 128, 1) == 0
+    assert v2(1, 1 << 16, 2, 1 << 22, 128, 1) == 3  # grid
+    assert v2(1, 4, 2, 8, 128, 1, ws=None) == 4     # no workspace
+    assert v2(1, 4, 2, 8, 128, 1, nbytes=v2ws - 1) == 4
+    assert v2(1, 4, 2, 8, 128, 1, ws=0x40008) == 4  # misaligned workspace
     need = da.diffattn_decode_workspace_bytes(2, 4, 2, 1000, 128)
     assert need > 0
     assert da.diffattn_decode_workspace_bytes(2, 3, 2, 1000, 128) == 0
@@ -117,6 +123,15 @@ def test_v2_and_decode_host_validation(da):
     assert dec(0x30000, need, P=3) == 2
     assert dec(0x30000, need, P=16, Hkv=1) == 3              # 32 query heads on one KV head
     assert dec(0x30000, need, L=0) == 2
+
+
+def test_v2_workspace_size_formula(da):
+    # 16-bit V copy rounded up to 256 bytes, then 4 flag bytes per 32-key tile of each KV head
+    assert da.diffattn_fwd_v2_workspace_bytes(1, 1, 1, 128) == 256 + 4
+    assert da.diffattn_fwd_v2_workspace_bytes(2, 8, 8192, 128) == 2 * 8 * 8192 * 256 + 2 * 8 * 256 * 4
+    assert da.diffattn_fwd_v2_workspace_bytes(1, 2, 33, 128) == 2 * 33 * 256 + 2 * 2 * 4
+    assert da.diffattn_fwd_v2_workspace_bytes(1, 2, 33, 64) == 0
+    assert da.diffattn_fwd_v2_workspace_bytes(0, 2, 33, 128) == 0
 
 
 def test_decode_workspace_size_formula(da):
@@ -175,7 +190,7 @@ def test_window_host_validation(da):
     t5 = [_t() for _ in range(5)]
     lam2 = _lam(dl=128)
     w2 = lambda window, P=4, Hkv=2: lib.diffattn_fwd_v2_window(
-        *t5, 1, P, Hkv, 8, 128, 1, ctypes.byref(lam2), window, None)
+        *t5, 1, P, Hkv, 8, 128, 1, ctypes.byref(lam2), window, 0x40000, 1 << 20, None)
     assert w2(0) == 2
     assert w2(5, P=3) == 2                 # P % Hkv
     # the causal entry points reject nothing new
