@@ -38,6 +38,7 @@ struct PrefillParams {
   int32_t norm;          // V1: apply RMS norm + (1 - lambda_init) scale
   int32_t n_row_blocks;  // query row blocks per (batch, head group)
   int32_t pairs_per_kv;  // V2: P / Hkv
+  int32_t group_heads;   // V1: issue the heads 8 at a time (one per XCD), see the prefill kernel
   float scale_log2;      // log2(e) / sqrt(d)
   float scale;           // 1 / sqrt(d)
   float eps;
