@@ -92,6 +92,46 @@ def test_v2_values_beyond_fp16_range(da):
     assert worst <= 1.0
 
 
+def test_v2_workspace_contents_do_not_matter(da):
+    """The V2 workspace (V rewritten as fp16 plus one flag byte per region) is clobbered by each
+    call: a workspace full of garbage, one left by a call on other data (whose V tiles held values
+    beyond the fp16 range, so its flags were set) and a fresh one give bit-identical outputs, for
+    the causal and the windowed entry point."""
+    import torch
+
+    log("v2 workspace reuse")
+    big = wl.make_v2(1, 2, 1, 300, 128, "bf16", seed=31, layers=(24,))
+    vf = wl.as_f32(big["v"], "bf16").copy()
+    vf[0, 0, ::7, ::5] = 1.0e5     # a value beyond fp16 in every 16-key x 64-channel region
+    big["v"] = wl.f32_to_bf16_bits(vf)
+    t = wl.make_v2(1, 2, 1, 257, 128, "bf16", seed=5, layers=(24,))
+    need = max(da.diffattn_fwd_v2_workspace_bytes(1, 1, 300, 128),
+               da.diffattn_fwd_v2_workspace_bytes(1, 1, 257, 128))
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    lv = dev_lambda(t["lambda"][24])
+    first = {}
+    for window in (0, 70):
+        outs = []
+        for fill in ("fresh", "garbage", "previous"):
+            if fill == "fresh":
+                ws = None
+            elif fill == "garbage":
+                ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+            else:
+                ws = torch.zeros((need,), dtype=torch.uint8, device="cuda")
+                qb = dev(big["q"])
+                da.diffattn_fwd_v2(qb[:, 0::2], qb[:, 1::2], dev(big["k"]), dev(big["v"]),
+                                   *dev_lambda(big["lambda"][24]), layer=24, workspace=ws)
+            o = da.diffattn_fwd_v2(q[:, 0::2], q[:, 1::2], k, v, *lv, layer=24, window=window,
+                                   workspace=ws)
+            torch.cuda.synchronize()
+            outs.append(o.cpu())
+        assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2]), window
+        first[window] = outs[0]
+    st = compare.bf16_stats(first[0].float().numpy(), _oracle_v2(t, 24, True), normalise=True)
+    assert compare.bf16_ok(st), st
+
+
 def test_v2_lambda_zero_is_even_heads_attention(da):
     """lambda = 0 gives plain softmax attention of the even query heads."""
     import torch
