@@ -166,9 +166,12 @@ void prefill_kernel(const PrefillParams p) {
   const char* k2_base = static_cast<const char*>(p.k2) + 2 * (b * p.sk2.sb + kvh * p.sk2.sh);
   const char* v_base = F16PV ? static_cast<const char*>(p.vh) + vhead * N * (kDV * 2)
                              : static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + kvh * p.sv.sh);
-  // F16PV: the flag word of each 32-key tile of this KV head
-  const uint32_t* vflag_words = F16PV ? reinterpret_cast<const uint32_t*>(p.vflags) + vhead * ((N + kSBN - 1) / kSBN)
-                                      : nullptr;
+  // F16PV: the flag word of each 32-key tile of this KV head, read through the scalar cache (the
+  // words were written by the previous kernel and are constant here): a vector load would make the
+  // compiler wait on the vector-memory counter before using the word, and that counter also
+  // covers the tile DMA just issued, which would then land before the current tile is computed
+  typedef const __attribute__((address_space(4))) uint32_t const_u32;
+  const_u32* vflag_words = F16PV ? (const_u32*)(p.vflags) + vhead * ((N + kSBN - 1) / kSBN) : nullptr;
 
   // ---- tile loads.  Wave w issues the 1 KB DMA loads j = w + 4i of a K buffer (K1 then K2 in
   // V1) and of a V buffer.  Lane offsets are relative to the tile's first row, which moves into
@@ -196,9 +199,7 @@ void prefill_kernel(const PrefillParams p) {
   }
   // F16PV: flag word of the tile being computed and of the tile being loaded
   uint32_t fw_cur = 0, fw_next = 0;
-  auto load_flags = [&](int i) -> uint32_t {
-    return F16PV ? __builtin_amdgcn_readfirstlane(vflag_words[i]) : 0u;
-  };
+  auto load_flags = [&](int i) -> uint32_t { return F16PV ? vflag_words[i] : 0u; };
 
   auto issue_k = [&](int kt, int buf) {
     bf16* kb = smem + buf * C::KBUF;
