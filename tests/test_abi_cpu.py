@@ -112,6 +112,7 @@ def test_v2_and_decode_host_validation(da):
     assert v2(1, 4, 2, 8, 128, 1, ws=None) == 4     # no workspace
     assert v2(1, 4, 2, 8, 128, 1, nbytes=v2ws - 1) == 4
     assert v2(1, 4, 2, 8, 128, 1, ws=0x40008) == 4  # misaligned workspace
+    assert v2(1 << 9, 256, 128, 8, 128, 1) == 3  # B * Hkv beyond the conversion pass's grid
     need = da.diffattn_decode_workspace_bytes(2, 4, 2, 1000, 128)
     assert need > 0
     assert da.diffattn_decode_workspace_bytes(2, 3, 2, 1000, 128) == 0
