@@ -19,12 +19,13 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libdiffattn.so")
 
-SOURCES = ["abi.cpp", "fwd_v1_f32.hip", "prefill_bf16.hip", "decode_v2.hip", "decode_v1.hip", "bwd_v1.hip"]
+SOURCES = ["abi.cpp", "fwd_v1_f32.hip", "prefill_bf16.hip", "prefill_v2_bf16.hip", "decode_v2.hip", "decode_v1.hip", "bwd_v1.hip"]
 # Per-source extra flags.  The prefill kernels keep their MFMA accumulators in VGPRs: the online
 # softmax rescales them with vector ALU ops, and AGPR-resident accumulators cost a copy per use.
 # They also never produce a NaN of their own (masked scores are -inf, exp2(-inf) = 0), so the
 # compiler may drop the NaN-quieting canonicalisations it would otherwise put before each max.
 EXTRA_FLAGS = {"prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+               "prefill_v2_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
                "bwd_v1.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 ARCH = "gfx950"
 COMMON_FLAGS = [

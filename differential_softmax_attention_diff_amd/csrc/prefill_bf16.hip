@@ -1,25 +1,24 @@
-// Fused differential-attention prefill for gfx950: bf16 inputs, fp32 accumulation, bf16 out.
+// Fused V1 differential-attention prefill for gfx950: bf16 inputs, fp32 accumulation, bf16 out.
 //
 // What is computed (Ultralytics glossary "Differential Transformer", section "Cómo funciona la
-// atención diferencial"; ai-engineering.academy "Atención Diferencial (V2)", sections "La idea
-// diferencial" and "V1 vs V2: la diferencia"):
+// atención diferencial"; ai-engineering.academy "Atención Diferencial (V2)", section "La idea
+// diferencial"):
 //   two softmax branches  A_b = softmax(Q_b K_b^T / sqrt(d)),  O = A_1 V - lambda A_2 V,
-//   V1: y = (1 - lambda_init) O / sqrt(mean(O^2) + eps)   (per head, over the 128 channels),
-//   V2: branches are the two query heads of a pair over one shared KV head; y = O.
-// Neither map is ever written to memory.
+//   y = (1 - lambda_init) O / sqrt(mean(O^2) + eps)   (per head, over the 128 channels).
+// Neither map is ever written to memory.  (The V2 layout has its own kernel, prefill_v2_bf16.)
 //
 // Design (one pass over K/V per block of 64 query rows):
-//  * A 256-thread workgroup owns 64 query rows of one head (V1) or pair (V2).  Its four
-//    wavefronts are (branch, row half): each runs ONE softmax branch over 32 rows, so it holds
-//    64 fp32 accumulators (32 rows x 128 channels) and only its own branch's Q operand.  That
-//    keeps V1 at 128 VGPRs (4 waves per SIMD) and V2 at under 168 (3 per SIMD); the waves of
-//    different workgroups on a SIMD overlap one another's softmax and MFMA work.
+//  * A 256-thread workgroup owns 64 query rows of one head.  Its four wavefronts are (branch,
+//    row half): each runs ONE softmax branch over 32 rows, so it holds 64 fp32 accumulators
+//    (32 rows x 128 channels) and only its own branch's Q operand.  That keeps the kernel at 128
+//    VGPRs (4 waves per SIMD); the waves of different workgroups on a SIMD overlap one another's
+//    softmax and MFMA work.
 //  * Tiles of 32 keys stream global -> LDS through buffer loads that write LDS directly (issued
 //    from inline asm, see dma16), double buffered: the loads of tile t+1 are in flight during
 //    the MFMAs of tile t; one barrier per tile.  The buffer range check returns zeros past the
 //    last row.  LDS rows are XOR-swizzled for the 64-bank LDS (16-byte chunks of K by
-//    (row >> 1) & 7 for 128-byte rows or row & 15 for 256-byte rows, 32-byte chunks of V by
-//    2 (row & 3)): the MFMA operand reads are conflict-free (SQ_LDS_BANK_CONFLICT = 0).
+//    (row >> 1) & 7, 32-byte chunks of V by 2 (row & 3)): the MFMA operand reads are
+//    conflict-free (SQ_LDS_BANK_CONFLICT = 0).
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16.  Its accumulator
 //    gives each lane one query column and keys {8j + 4h + r}; split into two 16-key halves these
 //    are exactly the B operand P^T of O^T = V^T P^T.  The V^T operand comes straight from the
@@ -31,16 +30,11 @@
 //    exact max is taken, the accumulators rescaled and the weights formed again.  The row sums
 //    add the rounded weights the MFMA consumes (v_dot2 of packed pairs against 1).
 //  * Epilogue: the branch-2 wave of a row half writes lambda acc_2 / l_2 to LDS; the branch-1
-//    wave forms acc_1 / l_1 minus it, applies the V1 RMS norm and scale, and stores bf16 (RNE).
+//    wave forms acc_1 / l_1 minus it, applies the RMS norm and scale, and stores bf16 (RNE).  The
+//    training forward also stores each branch's O_b and base-2 log-sum-exp.
 //  * Causal: a wave computes tiles up to its last visible key and then only helps load; only
-//    tiles crossing the diagonal or the ragged end are masked element by element.  Row blocks
-//    are issued heaviest first; all row blocks of a head (V1) or all pairs of a KV head (V2)
-//    land on one XCD.
-//  * F16PV (V2): P.V runs on the fp16 MFMA (P and V rounded to fp16, 11 significant bits instead
-//    of bf16's 8).  v2_values_kernel rewrites V once per call as fp16, region by region (16 keys
-//    x 64 channels), keeping bf16 where a region holds a value beyond the fp16 range, with one
-//    flag byte per region; the prefill streams those tiles like any other and reads a tile's four
-//    flags as one word, and a set flag sends the wave to a bf16 P.V loop from that tile on.
+//    tiles crossing the diagonal, the window's lower edge or the ragged end are masked element
+//    by element.  Row blocks are issued heaviest first; all row blocks of a head land on one XCD.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -54,15 +48,14 @@ using namespace tile;
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for the running max
 constexpr float kCapSum = 4096.f;    // largest lane weight sum per tile (2^12) before the max moves
-constexpr float kF16Max = 65504.f;   // largest fp16 magnitude
 constexpr int kSBN = 32;  // keys per tile
 // Tile buffers in LDS.  Three (loads two tiles ahead) measured 7 % slower for V1: 48 KB per
 // workgroup allows 3 workgroups per CU instead of 4, and load latency was not the limit.
 constexpr int kStagesV1 = 2;
 
-template <int DQK, bool V2, int NS>
+template <int DQK, int NS>
 struct SCfg {
-  static constexpr int NK = V2 ? 1 : 2;                 // K tensors per tile (V2: one shared K)
+  static constexpr int NK = 2;                          // K tensors per tile (K_1, K_2)
   static constexpr int K_ELEMS = kSBN * DQK;            // one K tensor tile
   static constexpr int KBUF = NK * K_ELEMS;             // one K buffer (all K tensors)
   static constexpr int VBUF = kSBN * kDV;               // one V buffer
@@ -72,23 +65,13 @@ struct SCfg {
   static constexpr int SMEM = NS * (KBUF + VBUF);       // [K0 .. K(NS-1) | V0 .. V(NS-1)]
 };
 
-// 8 packed fp16 values -> 8 packed bf16 values (RNE)
-__device__ __forceinline__ u32x4 f16x8_to_bf16x8(u32x4 x) {
-  const f16x8 h = __builtin_bit_cast(f16x8, x);
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (bf16)(float)h[i];
-  return __builtin_bit_cast(u32x4, r);
-}
-
-template <int DQK, bool V2, bool F16PV, int NS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(V2 ? 3 : 4)))
+template <int DQK, int NS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_kernel(const PrefillParams p) {
-  using C = SCfg<DQK, V2, NS>;
+  using C = SCfg<DQK, NS>;
   constexpr int BM = 64;
   __shared__ __attribute__((aligned(1024))) bf16 smem[C::SMEM];
   static_assert(C::SMEM * 2 >= 2 * 64 * 64 * 4, "epilogue exchange must fit the tile buffers");
-  static_assert(!F16PV || NS == 2, "F16PV keeps the flags of one tile ahead");
   constexpr uint32_t kKB = C::KBUF * 2, kVB = C::VBUF * 2;  // bytes per K / V buffer
 
   const int tid = threadIdx.x;
@@ -99,16 +82,16 @@ void prefill_kernel(const PrefillParams p) {
   const int c = lane & 31;
   const int hh = lane >> 5;
   // Blocks are dealt to the 8 XCDs round-robin by linear index and blockIdx.x runs fastest, so
-  // every row block of one head (V1, when 8 divides B*H), or of all pairs over one KV head (V2,
-  // when 8 divides B*Hkv), lands on the same XCD: a head's K/V is shared through one L2.  Row
-  // blocks go heaviest first over all heads, which keeps the causal tail short (a head-major
-  // order measured slower despite 6x less HBM fetch).  Long V1 sequences (group_heads) take the
+  // every row block of one head (when 8 divides B*H) lands on the same XCD: a head's K/V is
+  // shared through one L2.  Row blocks go heaviest first over all heads, which keeps the causal
+  // tail short (a head-major order measured slower despite 6x less HBM fetch).  Long sequences
+  // (group_heads) take the
   // heads 8 at a time instead, one per XCD, heaviest row block first within the group: each XCD
   // then streams one head's K/V at a time, and a group's tail is short next to its thousands of
   // row blocks (at N = 128K 4.5 % faster; at N = 4K the grouped order's tail cost 9 %).
   int rb = p.n_row_blocks - 1 - (int)blockIdx.y;  // heaviest row block first
   int hx = blockIdx.x;
-  if (!V2 && p.group_heads) {
+  if (p.group_heads) {
     const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     const int64_t gsz = 8 * (int64_t)p.n_row_blocks;
     const int j = (int)(lin % gsz);
@@ -119,19 +102,8 @@ void prefill_kernel(const PrefillParams p) {
   const int wrow = row0 + 32 * rh;
   const int N = p.N;
 
-  int b, kvh, qh;
-  if (!V2) {
-    b = hx / p.heads;
-    qh = hx % p.heads;
-    kvh = qh;
-  } else {
-    const int bk = p.B * p.Hkv;
-    const int i = blockIdx.x / bk;
-    const int rem = blockIdx.x % bk;
-    b = rem / p.Hkv;
-    kvh = rem % p.Hkv;
-    qh = kvh * p.pairs_per_kv + i;
-  }
+  const int b = hx / p.heads;
+  const int qh = hx % p.heads;
 
 
   // ---- this wave's Q^T operand (its own branch): lane holds row wrow + c, cols 16t + 8hh .. +7
@@ -159,19 +131,10 @@ void prefill_kernel(const PrefillParams p) {
   const int t0_wave = p.window > 0 ? max(t_begin, max(0, wrow - p.window + 1) / kSBN) : 0;
 
   const uint32_t k1_row = (uint32_t)(p.sk1.sn * 2), k2_row = (uint32_t)(p.sk2.sn * 2);
-  // F16PV: V comes from the fp16 copy, contiguous rows of 256 bytes
-  const int64_t vhead = (int64_t)b * p.Hkv + kvh;
-  const uint32_t v_row = F16PV ? (uint32_t)(kDV * 2) : (uint32_t)(p.sv.sn * 2);
-  const char* k1_base = static_cast<const char*>(p.k1) + 2 * (b * p.sk1.sb + kvh * p.sk1.sh);
-  const char* k2_base = static_cast<const char*>(p.k2) + 2 * (b * p.sk2.sb + kvh * p.sk2.sh);
-  const char* v_base = F16PV ? static_cast<const char*>(p.vh) + vhead * N * (kDV * 2)
-                             : static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + kvh * p.sv.sh);
-  // F16PV: the flag word of each 32-key tile of this KV head, read through the scalar cache (the
-  // words were written by the previous kernel and are constant here): a vector load would make the
-  // compiler wait on the vector-memory counter before using the word, and that counter also
-  // covers the tile DMA just issued, which would then land before the current tile is computed
-  typedef const __attribute__((address_space(4))) uint32_t const_u32;
-  const_u32* vflag_words = F16PV ? (const_u32*)(p.vflags) + vhead * ((N + kSBN - 1) / kSBN) : nullptr;
+  const uint32_t v_row = (uint32_t)(p.sv.sn * 2);
+  const char* k1_base = static_cast<const char*>(p.k1) + 2 * (b * p.sk1.sb + qh * p.sk1.sh);
+  const char* k2_base = static_cast<const char*>(p.k2) + 2 * (b * p.sk2.sb + qh * p.sk2.sh);
+  const char* v_base = static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + qh * p.sv.sh);
 
   // ---- tile loads.  Wave w issues the 1 KB DMA loads j = w + 4i of a K buffer (K1 then K2 in
   // V1) and of a V buffer.  Lane offsets are relative to the tile's first row, which moves into
@@ -197,9 +160,6 @@ void prefill_kernel(const PrefillParams p) {
     const int lcol = ((((slot >> 1) ^ (2 * (row & 3)))) << 4) + ((slot & 1) << 3);
     v_lane[i] = (uint32_t)row * v_row + lcol * 2;
   }
-  // F16PV: flag word of the tile being computed and of the tile being loaded
-  uint32_t fw_cur = 0, fw_next = 0;
-  auto load_flags = [&](int i) -> uint32_t { return F16PV ? vflag_words[i] : 0u; };
 
   auto issue_k = [&](int kt, int buf) {
     bf16* kb = smem + buf * C::KBUF;
@@ -240,7 +200,7 @@ void prefill_kernel(const PrefillParams p) {
   //  V^T operand db: two transposing reads; in each 16-lane group lane j addresses row
   //  4 hh + j / 4 (plus 16 u, and 8 for the upper read), channels 32 db + 16 dh + 4 (j % 4),
   //  whose 32-byte chunk db ^ (row & 3) puts it at v_ad ^ 64 db.
-  uint32_t k_ad = 2u * ((V2 ? 0 : br * C::K_ELEMS) + k_off<DQK>(c, 8 * hh));
+  uint32_t k_ad = 2u * (br * C::K_ELEMS + k_off<DQK>(c, 8 * hh));
   uint32_t v_ad;
   {
     const int j = lane & 15, dh = (lane >> 4) & 1;
@@ -283,33 +243,23 @@ void prefill_kernel(const PrefillParams p) {
   };
   // weights exp2((s - m) log2(e) / sqrt(d)) for the reference max m, rounded to the two packed
   // P operands (16 keys each); tl gets the lane's sum of the rounded weights
-  using POp = std::conditional_t<F16PV, f16x8, bf16x8>;
   // (s is overwritten by the weights; the rare slow path forms the scores again from LDS)
-  auto weights = [&](f32x16& e, POp& p0, POp& p1, float& tl, auto half_tag) {
-    constexpr bool kHalf = decltype(half_tag)::value;
+  auto weights = [&](f32x16& e, bf16x8& p0, bf16x8& p1, float& tl) {
     const float nm = -mrun * sl2;
 #pragma unroll
     for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(e[r], sl2, nm));
     tl = 0.f;
-    if constexpr (kHalf) {
-      p0 = __builtin_bit_cast(POp, cvt8h_sum(e, 0, tl));
-      p1 = __builtin_bit_cast(POp, cvt8h_sum(e, 8, tl));
-    } else {
-      p0 = __builtin_bit_cast(POp, cvt8_sum(e, 0, tl));
-      p1 = __builtin_bit_cast(POp, cvt8_sum(e, 8, tl));
-    }
+    p0 = cvt8_sum(e, 0, tl);
+    p1 = cvt8_sum(e, 8, tl);
   };
 
   // One tile of this wave's branch.  The softmax keeps a reference max m per row that moves only
   // when needed: the weights of a tile are formed against the current m, and only if some lane's
   // weight sum exceeds 2^kCap (a score beyond m + kCap in exp2 units, or the very first tile,
   // whose m is still -1e30) does the tile's exact row max get taken, the accumulators rescaled and
-  // the weights formed again.  Every weight the MFMA sees is then at most 2^kCap, so fp16 P
-  // cannot overflow.  softmax(s) does not depend on m, so the result is the same as with an exact
-  // running max.
-  auto compute_tile = [&](int i, auto slow_tag) {
-    constexpr bool kSlow = decltype(slow_tag)::value;
-    constexpr bool kHalf = F16PV && !kSlow;
+  // the weights formed again.  softmax(s) does not depend on m, so the result is the same as
+  // with an exact running max.
+  auto compute_tile = [&](int i) {
     const int kt = i * kSBN;
     const int buf = i % NS;
     const uint32_t kb = k_ad + buf * kKB;  // this tile's buffers (the swizzle XORs touch bits < 13)
@@ -318,9 +268,9 @@ void prefill_kernel(const PrefillParams p) {
     f32x16 s = scores(kb);
     __builtin_amdgcn_s_setprio(0);
     mask(s, kt);
-    POp p0, p1;
+    bf16x8 p0, p1;
     float tl;
-    weights(s, p0, p1, tl, std::integral_constant<bool, kHalf>{});
+    weights(s, p0, p1, tl);
     if (__any(!(tl <= kCapSum))) {
       // the K tile of this step is still in its buffer: form the scores again
       __builtin_amdgcn_s_setprio(1);
@@ -337,7 +287,7 @@ void prefill_kernel(const PrefillParams p) {
       lrun *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[db] *= alpha;
-      weights(s, p0, p1, tl, std::integral_constant<bool, kHalf>{});
+      weights(s, p0, p1, tl);
     }
     lrun += tl;
 
@@ -345,23 +295,13 @@ void prefill_kernel(const PrefillParams p) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const POp pp = u == 0 ? p0 : p1;
+      const bf16x8 pp = u == 0 ? p0 : p1;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const u32x2 lo = v_read(vb, db, u, 0);
         const u32x2 hi = v_read(vb, db, u, 1);
-        u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
-        if constexpr (kHalf) {
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a4), pp, acc[db], 0, 0, 0);
-        } else {
-          // bf16 P.V; on the F16PV slow path the fp16 regions are widened back to bf16 (exact for
-          // every value fp16 holds with 8 or more significant bits)
-          if constexpr (kSlow) {
-            if (((fw_cur >> (8 * (2 * u + (db >> 1)))) & 0xffu) == 0u) a4 = f16x8_to_bf16x8(a4);
-          }
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
-                                                           __builtin_bit_cast(bf16x8, pp), acc[db], 0, 0, 0);
-        }
+        const u32x4 a4 = {lo[0], lo[1], hi[0], hi[1]};
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pp, acc[db], 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -369,16 +309,13 @@ void prefill_kernel(const PrefillParams p) {
 
   // ---- main loop: loads of tile t+1 are in flight during the MFMAs of tile t.  A wave computes
   // the tiles up to its last visible key, then only helps load and meets the barriers, so that
-  // the loop that carries the accumulators has no path around them.  F16PV: from the first tile
-  // with a bf16 region on, a wave stays on the bf16 path, in a loop of its own so that the
-  // accumulators never merge from two paths inside one loop.
-  auto tile_big = [&](int) { return F16PV && fw_cur != 0u; };
+  // the loop that carries the accumulators has no path around them.
   // Iteration i loads tile i + NS - 1 into the buffer tile i - 1 used, computes tile i, and waits
   // until tile i + 1 has landed: with NS > 2 the loads of the tiles after it stay in flight
   // (vmcnt counts this wave's outstanding buffer loads, which complete in order).
   constexpr int kLoadsPerTile = C::NK * KPW + VPW;  // DMA instructions per wave per tile
   auto wait_next = [&](int i) {
-    if constexpr (NS == 2 || F16PV) {
+    if constexpr (NS == 2) {
       __builtin_amdgcn_s_waitcnt(0);
     } else {
       static_assert(NS == 3, "vmcnt for one younger tile in flight");
@@ -386,72 +323,52 @@ void prefill_kernel(const PrefillParams p) {
       else __builtin_amdgcn_s_waitcnt(0);
     }
   };
-  auto step = [&](int i, auto slow_tag) {
-    const int ahead = i + NS - 1;
-    const bool more = ahead < ntiles;
-    if (more) {
-      issue_tile(ahead);
-      fw_next = load_flags(ahead);
-    }
-    compute_tile(i, slow_tag);
+  auto step = [&](int i) {
+    if (i + NS - 1 < ntiles) issue_tile(i + NS - 1);
+    compute_tile(i);
     wait_next(i);
     __syncthreads();
-    fw_cur = fw_next;
   };
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) {
     if (t_begin + i < ntiles) issue_tile(t_begin + i);
   }
-  if constexpr (NS == 2 || F16PV) {
+  if constexpr (NS == 2) {
     __builtin_amdgcn_s_waitcnt(0);
   } else {
     if (t_begin + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kLoadsPerTile | (7 << 4) | (15 << 8));
     else __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
-  if (t_begin < ntiles) fw_cur = load_flags(t_begin);
   // tiles before this wave's window only need its share of the loads and the barriers
   auto help = [&](int i) {
-    const int ahead = i + NS - 1;
-    if (ahead < ntiles) {
-      issue_tile(ahead);
-      fw_next = load_flags(ahead);
-    }
+    if (i + NS - 1 < ntiles) issue_tile(i + NS - 1);
     wait_next(i);
     __syncthreads();
-    fw_cur = fw_next;
   };
   int it = t_begin;
   for (; it < t0_wave; ++it) help(it);
-  for (; it < nt_wave; ++it) {
-    if (tile_big(it)) break;
-    step(it, std::false_type{});
-  }
-  if constexpr (F16PV) {
-    for (; it < nt_wave; ++it) step(it, std::true_type{});
-  }
+  for (; it < nt_wave; ++it) step(it);
   for (; it < ntiles; ++it) help(it);
 
   // ---- epilogue: branch-2 waves publish lambda acc_2 / l_2; branch-1 waves finish the rows
   const float lam = head_lambda(p.lam, qh, lane);
   if (p.lam.out != nullptr && b == 0 && rb == 0 && w == 0 && lane == 0) p.lam.out[qh] = lam;
-  if constexpr (!V2) {
-    // training forward: this branch's normalised output and log-sum-exp (base 2) per row
-    if (p.stash_o != nullptr && wave_has_rows && wrow + c < N) {
-      const float l = pair_sum(lrun);
-      const float inv = 1.f / l;
-      const int64_t row = (((int64_t)br * p.B + b) * p.heads + qh) * N + wrow + c;
-      float* o = p.stash_o + row * kDV;
+  // training forward: this branch's normalised output and log-sum-exp (base 2) per row
+  if (p.stash_o != nullptr && wave_has_rows && wrow + c < N) {
+    const float l = pair_sum(lrun);
+    const float inv = 1.f / l;
+    const int64_t row = (((int64_t)br * p.B + b) * p.heads + qh) * N + wrow + c;
+    float* o = p.stash_o + row * kDV;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 x = {acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv, acc[db][4 * j + 2] * inv,
-                           acc[db][4 * j + 3] * inv};
-          *reinterpret_cast<f32x4*>(o + db * 32 + 8 * j + 4 * hh) = x;
-        }
-      if (hh == 0) p.stash_lse[row] = mrun * sl2 + __log2f(l);
-    }
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 x = {acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv, acc[db][4 * j + 2] * inv,
+                         acc[db][4 * j + 3] * inv};
+        *reinterpret_cast<f32x4*>(o + db * 32 + 8 * j + 4 * hh) = x;
+      }
+    if (hh == 0) p.stash_lse[row] = mrun * sl2 + __log2f(l);
   }
   float* xb = reinterpret_cast<float*>(smem) + rh * (64 * 64);
   if (br == 1 && wave_has_rows) {
@@ -475,7 +392,7 @@ void prefill_kernel(const PrefillParams p) {
       ss = fmaf(x, x, ss);
     }
   float rs = 1.f;
-  if (!V2 && p.norm) {
+  if (p.norm) {
     ss = pair_sum(ss);
     rs = p.out_scale * rsqrtf(ss * (1.f / kDV) + p.eps);
   }
@@ -493,48 +410,6 @@ void prefill_kernel(const PrefillParams p) {
     }
 }
 
-// V2 values for the fp16 P.V: one workgroup per 32-key tile of a KV head, one wave per region
-// of 16 keys x 64 channels (rows 16 (w >> 1) + q / 8, channels 64 (w & 1) + 8 (q % 8) for
-// q = lane + 64 s).  A region is written as fp16 unless it holds a value beyond the fp16 range
-// (then as its bf16 bits), and its flag byte says which.  Rows past N are neither read (the
-// buffer range check returns zeros) nor written.
-__global__ __launch_bounds__(kThreads) void v2_values_kernel(const PrefillParams p) {
-  const int tile = blockIdx.x;
-  const int bh = blockIdx.y;  // b * Hkv + KV head
-  const int b = bh / p.Hkv, kvh = bh % p.Hkv;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int N = p.N;
-  const int kt = tile * kSBN;
-  const uint32_t v_row = (uint32_t)(p.sv.sn * 2);
-  const char* vsrc = static_cast<const char*>(p.v) + 2 * (b * p.sv.sb + kvh * p.sv.sh);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vsrc + (size_t)kt * v_row, (uint32_t)(N - kt) * v_row);
-  u32x4 x[2];
-  int row[2], col[2];
-  float mx = 0.f;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int q = lane + 64 * s;
-    row[s] = 16 * (w >> 1) + (q >> 3);
-    col[s] = 64 * (w & 1) + 8 * (q & 7);
-    x[s] = bload16(rv, (uint32_t)row[s] * v_row + col[s] * 2);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(x[s][m])), fabsf(bf16_hi(x[s][m]))));
-  }
-  const bool big = __any(mx > kF16Max);
-  bf16* dst = static_cast<bf16*>(p.vh) + (int64_t)bh * N * kDV;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    u32x4 y = x[s];
-    if (!big) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) y[m] = pack_h2(bf16_lo(x[s][m]), bf16_hi(x[s][m]));
-    }
-    if (kt + row[s] < N) store16(dst + (int64_t)(kt + row[s]) * kDV + col[s], y);
-  }
-  if (lane == 0) p.vflags[((int64_t)bh * gridDim.x + tile) * 4 + w] = big ? 1 : 0;
-}
-
 }  // namespace
 
 hipError_t launch_v1_bf16(const PrefillParams& p, hipStream_t stream) {
@@ -542,17 +417,7 @@ hipError_t launch_v1_bf16(const PrefillParams& p, hipStream_t stream) {
   q.n_row_blocks = (p.N + 63) / 64;
   q.group_heads = ((p.B * p.heads) % 8 == 0 && q.n_row_blocks >= 512) ? 1 : 0;
   const dim3 grid(p.B * p.heads, q.n_row_blocks);
-  hipLaunchKernelGGL((prefill_kernel<64, false, false, kStagesV1>), grid, dim3(kThreads), 0, stream, q);
-  return hipGetLastError();
-}
-
-hipError_t launch_v2_bf16(const PrefillParams& p, hipStream_t stream) {
-  PrefillParams q = p;
-  q.pairs_per_kv = p.heads / p.Hkv;
-  q.n_row_blocks = (p.N + 63) / 64;
-  hipLaunchKernelGGL(v2_values_kernel, dim3((p.N + kSBN - 1) / kSBN, p.B * p.Hkv), dim3(kThreads), 0, stream, q);
-  const dim3 grid(p.B * p.heads, q.n_row_blocks);
-  hipLaunchKernelGGL((prefill_kernel<128, true, true, 2>), grid, dim3(kThreads), 0, stream, q);
+  hipLaunchKernelGGL((prefill_kernel<64, kStagesV1>), grid, dim3(kThreads), 0, stream, q);
   return hipGetLastError();
 }
 
