@@ -49,6 +49,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "prefill_bf16.hip"),
+    "prefill_v2": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "prefill_v2_bf16.hip"),
     "decode": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "decode_v2.hip"),
     "decode_v1": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "decode_v1.hip"),
     "bwd": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "bwd_v1.hip"),
@@ -124,7 +125,7 @@ def bench_v1(da, torch, steps, warmup):
                      "traffic": measured_traffic("v1_prefill_4k", "prefill"),
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
-                     "kernel": "prefill_kernel<64,false,false>"},
+                     "kernel": "prefill_kernel<64,2>"},
     }
     return res, (cfg, t)
 
@@ -152,10 +153,10 @@ def bench_v2(da, torch, steps, warmup):
                    "N": N, "D": D, "causal": True, "layer": layer, "dtype": "bf16"},
         "roofline": {"bound": "mfma", "achieved": round(tf_alg, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf_alg / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("v2_prefill_8k", "prefill"),
+                     "traffic": measured_traffic("v2_prefill_8k", "prefill_v2"),
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
-                     "kernel": "v2_values_kernel + prefill_kernel<128,true,true>"},
+                     "kernel": "v2_values_kernel + prefill_v2_kernel"},
     }
 
 
@@ -194,7 +195,7 @@ def bench_long(da, torch, steps, warmup):
                      "traffic": measured_traffic("v1_long_128k", "prefill"),
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
-                     "kernel": "prefill_kernel<64,false,false>"},
+                     "kernel": "prefill_kernel<64,2>"},
     }
 
 
@@ -253,7 +254,7 @@ def bench_swa(da, torch, steps, warmup):
                      "traffic": measured_traffic("v1_swa_4k", "prefill"),
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
-                     "kernel": "prefill_kernel<64,false,false> (sliding window)"},
+                     "kernel": "prefill_kernel<64,2> (sliding window)"},
     }
 
 
