@@ -139,6 +139,23 @@ def test_v1_bf16_workload_4k_sampled_rows(da):
             assert compare.bf16_ok(st), (b, h, st)
 
 
+def test_v1_bf16_grouped_head_order_ragged(da):
+    """From 512 row blocks per head on (N >= 32705) with 8 dividing B*H, the prefill issues the
+    heads 8 at a time, one per XCD; here two batches of 8 heads (two groups) at a ragged length
+    just past that threshold, non-trivial lambda, checked on sampled rows of every head."""
+    N = 512 * 64 + 37
+    t = wl.make_v1(2, 8, N, 64, "bf16", seed=4242, layers=(5,))
+    got = _run_v1(da, t, "bf16", 5)
+    assert np.isfinite(got).all()
+    rows = sample_rows(N, 12, seed=9, extra=(0, 63, 64, N - 38, N - 37, N - 2, N - 1))
+    ref = _oracle_v1(t, "bf16", 5, rows=rows)
+    for b in (0, 1):
+        for h in range(8):
+            st = compare.bf16_stats(got[b, h, rows], ref[b, h])
+            assert compare.bf16_ok(st), (b, h, st)
+    log(f"  grouped order N={N}: 16 heads ok")
+
+
 @pytest.mark.timeout(600)
 def test_v1_bf16_long_context_128k_needles(da):
     """V1 long-context workload (B=1, H=16, N=131072) with 6 planted needle keys per head, at
