@@ -258,8 +258,11 @@ void prefill_kernel(const PrefillParams p) {
   // weight sum exceeds 2^kCap (a score beyond m + kCap in exp2 units, or the very first tile,
   // whose m is still -1e30) does the tile's exact row max get taken, the accumulators rescaled and
   // the weights formed again.  softmax(s) does not depend on m, so the result is the same as
-  // with an exact running max.
-  auto compute_tile = [&](int i) {
+  // with an exact running max.  kFirst: the wave's first tile, whose m starts at this tile's
+  // exact row max straight from its scores (nothing is accumulated yet, so nothing rescales, and
+  // every weight is at most 1).
+  auto compute_tile = [&](int i, auto first_tag) {
+    constexpr bool kFirst = decltype(first_tag)::value;
     const int kt = i * kSBN;
     const int buf = i % NS;
     const uint32_t kb = k_ad + buf * kKB;  // this tile's buffers (the swizzle XORs touch bits < 13)
@@ -268,10 +271,16 @@ void prefill_kernel(const PrefillParams p) {
     f32x16 s = scores(kb);
     __builtin_amdgcn_s_setprio(0);
     mask(s, kt);
+    if constexpr (kFirst) {
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mrun = fmaxf(mrun, pmax(mx));
+    }
     bf16x8 p0, p1;
     float tl;
     weights(s, p0, p1, tl);
-    if (__any(!(tl <= kCapSum))) {
+    if (!kFirst && __any(!(tl <= kCapSum))) {
       // the K tile of this step is still in its buffer: form the scores again
       __builtin_amdgcn_s_setprio(1);
       s = scores(kb);
@@ -323,9 +332,9 @@ void prefill_kernel(const PrefillParams p) {
       else __builtin_amdgcn_s_waitcnt(0);
     }
   };
-  auto step = [&](int i) {
+  auto step = [&](int i, auto first_tag) {
     if (i + NS - 1 < ntiles) issue_tile(i + NS - 1);
-    compute_tile(i);
+    compute_tile(i, first_tag);
     wait_next(i);
     __syncthreads();
   };
@@ -348,7 +357,8 @@ void prefill_kernel(const PrefillParams p) {
   };
   int it = t_begin;
   for (; it < t0_wave; ++it) help(it);
-  for (; it < nt_wave; ++it) step(it);
+  if (it < nt_wave) step(it++, std::true_type{});
+  for (; it < nt_wave; ++it) step(it, std::false_type{});
   for (; it < ntiles; ++it) help(it);
 
   // ---- epilogue: branch-2 waves publish lambda acc_2 / l_2; branch-1 waves finish the rows

@@ -291,8 +291,9 @@ void prefill_v2_kernel(const PrefillParams p) {
   // One tile, both heads: scores, weights (moving a head's m when some weight would exceed
   // 2^12), then O^T += V^T P^T with each V^T operand feeding both heads' MFMAs.  kSlow: the bf16
   // P.V path, taken from the first tile holding a bf16 V region on.
-  auto compute_tile = [&](int i, auto slow_tag) {
+  auto compute_tile = [&](int i, auto slow_tag, auto first_tag) {
     constexpr bool kSlow = decltype(slow_tag)::value;
+    constexpr bool kFirst = decltype(first_tag)::value;
     const int kt = i * 32;
     const uint32_t off = (uint32_t)(i & 1) * kStageBytes;
     const uint32_t kb = ka + off, vb = va + off;
@@ -303,13 +304,23 @@ void prefill_v2_kernel(const PrefillParams p) {
     scores2(kb, sa, sbb);
     __builtin_amdgcn_s_setprio(0);
     if (masked) { mask(sa, kt); mask(sbb, kt); }
+    if constexpr (kFirst) {
+      // the wave's first tile: each head's m starts at this tile's exact row max (nothing is
+      // accumulated yet, so nothing rescales, and every weight is at most 1)
+      auto tile_max = [](const f32x4 (&s)[2]) {
+        return fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+      };
+      ma = fmaxf(ma, row4_max(tile_max(sa)));
+      mb = fmaxf(mb, row4_max(tile_max(sbb)));
+    }
     using HT = std::integral_constant<bool, !kSlow>;
     float tla, tlb;
     u32x4 pa = weights(sa, ma, tla, HT{});
-    if (__any(!(tla <= kCapSum))) pa = move_max(kb, qa, kt, masked, ma, la, acca, tla, HT{});
+    if (!kFirst && __any(!(tla <= kCapSum))) pa = move_max(kb, qa, kt, masked, ma, la, acca, tla, HT{});
     la += tla;
     u32x4 pb = weights(sbb, mb, tlb, HT{});
-    if (__any(!(tlb <= kCapSum))) pb = move_max(kb, qb, kt, masked, mb, lb, accb, tlb, HT{});
+    if (!kFirst && __any(!(tlb <= kCapSum))) pb = move_max(kb, qb, kt, masked, mb, lb, accb, tlb, HT{});
     lb += tlb;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -350,20 +361,21 @@ void prefill_v2_kernel(const PrefillParams p) {
     __syncthreads();
     fw_cur = fw_next;
   };
-  auto step = [&](int i, auto slow_tag) {
+  auto step = [&](int i, auto slow_tag, auto first_tag) {
     if (i + 1 < ntiles) { issue_tile(i + 1); fw_next = load_flags(i + 1); }
-    compute_tile(i, slow_tag);
+    compute_tile(i, slow_tag, first_tag);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     fw_cur = fw_next;
   };
   int it = t_begin;
   for (; it < t0_wave; ++it) help(it);
+  if (it < nt_wave && fw_cur == 0u) step(it++, std::false_type{}, std::true_type{});
   for (; it < nt_wave; ++it) {
     if (fw_cur != 0u) break;
-    step(it, std::false_type{});
+    step(it, std::false_type{}, std::false_type{});
   }
-  for (; it < nt_wave; ++it) step(it, std::true_type{});
+  for (; it < nt_wave; ++it) step(it, std::true_type{}, std::false_type{});
   for (; it < ntiles; ++it) help(it);
 
   // ---- epilogue: out = O_a / l_a - lambda O_b / l_b; lane (n, g) holds row wrow + n, channels
