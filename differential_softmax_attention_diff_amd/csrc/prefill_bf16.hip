@@ -25,8 +25,8 @@
 //    row-major V tile through ds_read_b64_tr_b16 (a transposing LDS read: per 16-lane group, each
 //    lane receives one column of a 4-key x 16-channel block).
 //  * Online softmax without a per-tile max: weights exp2((s - m) log2(e)/sqrt(d)) are formed
-//    against a per-row reference max m that moves only when a lane's weight sum for the tile
-//    exceeds 2^12 (the first tile, where m is still -1e30, or a score jump); then the tile's
+//    against a per-row reference max m, set from the exact row max of the wave's first tile and
+//    moved only when a lane's weight sum for a tile exceeds 2^12 (a score jump); then the tile's
 //    exact max is taken, the accumulators rescaled and the weights formed again.  The row sums
 //    add the rounded weights the MFMA consumes (v_dot2 of packed pairs against 1).
 //  * Epilogue: the branch-2 wave of a row half writes lambda acc_2 / l_2 to LDS; the branch-1

@@ -25,9 +25,9 @@
 //    row n and keys 16 h + 4 g + r of key half h; read as k-slot 8 g + 4 h + r that is exactly
 //    the B operand P^T of O^T = V^T P^T, whose A operand takes V rows 4 g + r and 16 + 4 g + r
 //    from two transposing LDS reads (ds_read_b64_tr_b16).
-//  * Online softmax against a per-row reference max m that moves only when a lane's weight sum
-//    for the tile exceeds 2^12 (the first tile, where m is still -1e30, or a score jump): every
-//    weight the fp16 MFMA sees is then at most 2^12.  softmax(s) does not depend on m, so the
+//  * Online softmax against a per-row reference max m, set from the exact row max of the wave's
+//    first tile and moved only when a lane's weight sum for a tile exceeds 2^12 (a score jump):
+//    every weight the fp16 MFMA sees is then at most 2^12.  softmax(s) does not depend on m, so the
 //    result is that of an exact running max.  The row sums add the rounded weights.
 //  * A tile whose V regions include a bf16 one (a value beyond the fp16 range) sends the wave to
 //    a bf16 P.V loop from that tile on, where the fp16 regions are widened back to bf16 (exact
