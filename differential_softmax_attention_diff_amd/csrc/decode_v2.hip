@@ -50,7 +50,9 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
   const int grp = lane >> 4;
 
   // keys of this sequence (paged: its own length, clamped to the table's extent)
-  const int seq_len = PAGED ? min(max(p.seq_lens[b], 0), min(p.L, p.max_blocks << p.page_shift)) : p.L;
+  const int seq_len =
+      PAGED ? (int)min((int64_t)max(p.seq_lens[b], 0), min((int64_t)p.L, (int64_t)p.max_blocks << p.page_shift))
+            : p.L;
   // the sequence's 256-key blocks are dealt evenly to the splits, so that with per-sequence
   // lengths every split of a sequence gets the same share (empty only when it has fewer blocks
   // than splits)

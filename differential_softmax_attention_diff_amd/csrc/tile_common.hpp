@@ -78,7 +78,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Issued from inline asm so that the compiler does not treat it as aliasing every later LDS read
 // (it would otherwise wait for all outstanding DMA before each one, defeating the prefetch); the
 // kernels order these writes themselves with explicit vmcnt waits and barriers.  M0 holds the LDS
-// base; one wait state separates the M0 write from the DMA.
+// base (declared clobbered, so the compiler keeps nothing of its own there across the asm); one
+// wait state separates the M0 write from the DMA.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, uint32_t voff) {
   const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void*)lds;
   asm volatile(
@@ -87,7 +88,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16* lds, uint3
       "buffer_load_dwordx4 %1, %2, 0 offen lds"
       :
       : "s"(m0v), "v"(voff), "s"(r)
-      : "memory");
+      : "memory", "m0");
 }
 
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {

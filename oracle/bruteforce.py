@@ -14,11 +14,15 @@ import math
 
 
 def softmax(row):
-    """Softmax of a list of floats with the maximum subtracted first."""
-    m = max(row)
-    exps = [math.exp(x - m) for x in row]
-    s = sum(exps)
-    return [e / s for e in exps]
+    """Softmax of a list of floats through its log-normaliser.
+
+    log Z = top + log(sum_j exp(x_j - top)) with top the largest entry (shifting by it keeps every
+    exponential at most 1, the stability step of [L] "Implementación", step 1); each weight is then
+    exp(x_i - log Z).  ``math.fsum`` keeps the sum exactly rounded.
+    """
+    top = max(row)
+    log_z = top + math.log(math.fsum(math.exp(x - top) for x in row))
+    return [math.exp(x - log_z) for x in row]
 
 
 def dot(a, b):
