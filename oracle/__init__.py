@@ -27,6 +27,7 @@ from .diffattn_oracle import (  # noqa: F401
     branch_rows,
     rms_norm_rows,
     diff_attn_v1,
+    diff_attn_v1_layers,
     diff_attn_v2,
     diff_decode_v2,
     diff_decode_v1,

@@ -45,6 +45,7 @@ __all__ = [
     "branch_rows",
     "rms_norm_rows",
     "diff_attn_v1",
+    "diff_attn_v1_layers",
     "diff_attn_v2",
     "diff_decode_v2",
     "diff_decode_v1",
@@ -222,6 +223,35 @@ def diff_attn_v1(q1, q2, k1, k2, v, lam, lam_init: float, causal: bool = True,
             if norm:
                 o = rms_norm_rows(o, eps) * (1.0 - lam_init)
             out[bi, hi] = o
+    return out
+
+
+def diff_attn_v1_layers(q1, q2, k1, k2, v, lams, lam_inits, causal: bool = True,
+                        eps: float = 1e-5, rows=None, heads=None, batches=None, window: int = 0):
+    """V1 outputs of several layers that share Q1, Q2, K1, K2, V and differ only in lambda.
+
+    (A1 - lam A2) V = A1 V - lam (A2 V) by distributivity, so the two branch outputs A1 V and
+    A2 V are formed once per head and each layer's difference, RMS norm and (1 - lambda_init)
+    scale is applied to them ([L] "V1 vs V2: la diferencia" states the same identity: the V2
+    layout subtracts two heads' ordinary attention outputs and the math is unchanged).
+    ``lams`` is [n_layers, H] (one lambda per head and layer), ``lam_inits`` is [n_layers].
+    Returns float64 [n_layers, len(batches), len(heads), len(rows), 2d].
+    """
+    lams = np.asarray(lams, dtype=np.float64)
+    lam_inits = np.asarray(lam_inits, dtype=np.float64).reshape(-1)
+    if lams.ndim != 2 or lams.shape != (lam_inits.size, q1.shape[1]):
+        raise ValueError("lams must be [n_layers, H] with one lambda_init per layer")
+    b_list = range(q1.shape[0]) if batches is None else list(batches)
+    h_list = range(q1.shape[1]) if heads is None else list(heads)
+    rows = _rows_arg(rows, q1.shape[2])
+    out = np.empty((lam_inits.size, len(b_list), len(h_list), rows.size, v.shape[-1]),
+                   dtype=np.float64)
+    for bi, b in enumerate(b_list):
+        for hi, h in enumerate(h_list):
+            o1 = branch_rows(q1[b, h], k1[b, h], v[b, h], causal, rows, window)
+            o2 = branch_rows(q2[b, h], k2[b, h], v[b, h], causal, rows, window)
+            for li in range(lam_inits.size):
+                out[li, bi, hi] = rms_norm_rows(o1 - lams[li, h] * o2, eps) * (1.0 - lam_inits[li])
     return out
 
 

@@ -14,10 +14,19 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "diffattn.h")
 
 
+# tests/test_abi_sanitized.py re-runs this file against an AddressSanitizer + UBSan build of the
+# host layer, named by this variable; otherwise the in-tree library is checked
+SANITIZED_LIB = os.environ.get("DIFFATTN_SANITIZED_LIB")
+
+
 @pytest.fixture(scope="module")
 def da():
     import differential_softmax_attention_diff_amd as mod
 
+    if SANITIZED_LIB:
+        mod._LIB = mod.load_library(SANITIZED_LIB)
+        mod.LIB_PATH = SANITIZED_LIB
+        return mod
     if not os.path.exists(mod.LIB_PATH):
         pytest.fail("libdiffattn.so is not built (run __graft_entry__.build())")
     mod.load_library()

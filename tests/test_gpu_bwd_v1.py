@@ -2,19 +2,26 @@
 autograd and finite differences).
 
 Gradients have no fixed scale, so each (batch, head) slice of a gradient is divided by its oracle
-RMS before the bound is applied.  The bound comes from the arithmetic: the three gradient
-products take one operand each in bf16 (the upstream gradient through the norm, the
-probabilities, and the score gradient dS = P * (dP - D)), with unit roundoff u = 2^-9, and dS
-itself inherits the rounding of dO through dP.  The stash adds one more: the forward's bf16
-weights make O_b and the log-sum-exp agree only to about u, so the softmax Jacobian's subtraction
-leaves a residual of that order, largest on rows with few visible keys.  Each gradient entry is
-a sum over up to N such products whose exact value cancels (every row of dS sums to zero), so
-its rounding error, relative to the slice RMS, is a few u on average with tails of 10-30 u:
-re-running the oracle's float64 chain with those roundings (operands and stash) gives a
-normalised max error of 0.02-0.04 and an RMS of 0.0027 on these shapes, the kernel up to 0.057
-and 0.003.  The bar is BWD_MAX_TOL on the largest normalised error and BWD_RMS_TOL on its RMS,
-far below the O(1) error of a dropped term, a sign or a transposed operand.  The lambda-vector
-gradients are checked by _check_lambda_grads."""
+RMS before any bound is applied.  The bound comes from the arithmetic, made concrete by
+``tests/bwd_rounding_model.py``: a float64 model that rounds to bf16 exactly where the kernels do
+(the forward's weights against its reference max, from which the stash's O_b and log-sum-exp
+come; dO through the norm; the dV operand P_1 - lambda P_2; the score gradient P_b (dO V^T - Dt_b))
+and nowhere else.  On the seeded cases here that model alone reaches a normalised max error of
+0.057 (B=2 H=2 N=222 causal, dK_1 at key 2: rows with few visible keys, where nothing averages the
+roundings out) and an RMS of 0.0024-0.0030; with all four roundings switched off it equals the
+oracle to 1e-12.  Each gradient must therefore satisfy, per slice:
+
+* |kernel - model| / rms(oracle) <= BWD_MODEL_DIST everywhere: the kernel rounds where the model
+  says, and what is left is fp32 summation order and the hardware exp2, which now and then put a
+  value on the other side of a bf16 rounding boundary than the model does -- one bf16 step (at
+  most 2^-7 of the value) of one product term; measured up to 0.013 over the seeded cases, while
+  the max errors of kernel and model against the oracle agree to four decimals;
+* max |kernel - oracle| / rms(oracle) <= (the model's own max error) + BWD_MODEL_MARGIN;
+* that max <= BWD_MAX_TOL = 0.057 + 0.013, the model's worst case over the seeded cases plus the
+  margin, and the RMS of the ratio <= BWD_RMS_TOL.
+
+A dropped term, a sign or a transposed operand gives errors of order one on all three.  The
+lambda-vector gradients are checked by _check_lambda_grads."""
 
 import numpy as np
 import pytest
@@ -26,8 +33,10 @@ from tests.helpers import dev, dev_lambda, f64, log
 
 pytestmark = pytest.mark.gpu
 
-BWD_MAX_TOL = 8e-2
+BWD_MAX_TOL = 7e-2
 BWD_RMS_TOL = 1e-2
+BWD_MODEL_DIST = 2e-2
+BWD_MODEL_MARGIN = 1e-2
 
 
 @pytest.fixture(scope="module")
@@ -57,6 +66,48 @@ def _slice_stats(got, ref):
 
 def _ok(st):
     return st["finite"] and st["max_abs"] <= BWD_MAX_TOL and st["rms"] <= BWD_RMS_TOL
+
+
+def _dist(got, model, ref):
+    """max over a gradient of |got - model| / rms(ref), per (batch, head) slice (as _slice_stats)."""
+    g = got.reshape(got.shape[0] * got.shape[1], -1)
+    m = model.reshape(g.shape)
+    r = ref.reshape(g.shape)
+    rms_all = float(np.sqrt(np.mean(r * r)))
+    rms = np.maximum(np.sqrt(np.mean(r * r, axis=1, keepdims=True)), max(1e-3 * rms_all, 1e-6))
+    return float(np.max(np.abs(g - m) / rms))
+
+
+def check_gradients(g, ref, t, layer, dy, causal=True, window=0, max_tol=BWD_MAX_TOL):
+    """The bar described in the module docstring, for dQ_1, dQ_2, dK_1, dK_2 and dV; then the
+    lambda-vector gradients.  When a row sees a single key (N = 1 or a window of 1) each softmax
+    is the constant 1, dQ and dK vanish exactly, and the kernel's are bounded by 1e-5.  ``max_tol``
+    is the fixed cap on the normalised max error (BWD_MAX_TOL unless a test derives its own from
+    the model's error on its inputs)."""
+    from tests.bwd_rounding_model import model_backward
+
+    args = [f64(t[k]) for k in ("q1", "q2", "k1", "k2", "v")]
+    lam = oracle.lambda_value(*t["lambda"][layer], layer)
+    model = model_backward(*args, lam, oracle.lambda_init(layer), f64(dy), causal, 1e-5,
+                           window=window)
+    N = args[0].shape[2]
+    single_key = N == 1 or window == 1
+    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
+        if single_key and k != "dv":
+            assert np.max(np.abs(ref[k])) == 0.0
+            log(f"  {k} max |got| {np.max(np.abs(g[k])):.3e}")
+            assert np.max(np.abs(g[k])) <= 1e-5, k
+            continue
+        st = _slice_stats(g[k], ref[k])
+        mst = _slice_stats(model[k], ref[k])
+        dist = _dist(g[k], model[k], ref[k])
+        log(f"  {k} kernel {st['max_abs']:.4f}/{st['rms']:.4f} model {mst['max_abs']:.4f}/"
+            f"{mst['rms']:.4f} |kernel - model| {dist:.4f}")
+        assert st["finite"], k
+        assert dist <= BWD_MODEL_DIST, (k, dist)
+        assert st["max_abs"] <= mst["max_abs"] + BWD_MODEL_MARGIN, (k, st, mst)
+        assert st["max_abs"] <= max_tol and st["rms"] <= BWD_RMS_TOL, (k, st)
+    _check_lambda_grads(g, ref)
 
 
 def _check_lambda_grads(g, ref):
@@ -102,18 +153,7 @@ def test_bwd_v1_against_oracle(da, B, H, N, causal):
     out, g = _run(da, t, layer, causal, dy)
     ref = oracle.diff_attn_v1_backward(*(f64(t[k]) for k in ("q1", "q2", "k1", "k2", "v")),
                                        t["lambda"][layer], layer, f64(dy), causal, 1e-5)
-    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
-        if N == 1 and k != "dv":
-            # One visible key: each softmax is the constant 1, so dQ and dK vanish exactly; the
-            # kernel leaves only the fp32 difference of two summation orders of dO . O_b.
-            assert np.max(np.abs(ref[k])) == 0.0
-            log(f"  {k} max |got| {np.max(np.abs(g[k])):.3e}")
-            assert np.max(np.abs(g[k])) <= 1e-5, k
-            continue
-        st = _slice_stats(g[k], ref[k])
-        log(f"  {k} {st}")
-        assert _ok(st), (k, st)
-    _check_lambda_grads(g, ref)
+    check_gradients(g, ref, t, layer, dy, causal)
 
 
 def test_train_forward_output_equals_forward(da):
@@ -137,11 +177,7 @@ def test_bwd_v1_workload_slice(da):
     _, g = _run(da, t, layer, True, dy)
     ref = oracle.diff_attn_v1_backward(*(f64(t[k]) for k in ("q1", "q2", "k1", "k2", "v")),
                                        t["lambda"][layer], layer, f64(dy), True, 1e-5)
-    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
-        st = _slice_stats(g[k], ref[k])
-        log(f"  {k} {st}")
-        assert _ok(st), (k, st)
-    _check_lambda_grads(g, ref)
+    check_gradients(g, ref, t, layer, dy, True)
 
 
 def test_bwd_strided_inputs_match_contiguous(da):
@@ -237,16 +273,7 @@ def test_bwd_v1_window_against_oracle(da, B, H, N, window):
     ref = oracle.diff_attn_v1_backward(*(f64(t[k]) for k in ("q1", "q2", "k1", "k2", "v")),
                                        t["lambda"][layer], layer, f64(dy), True, 1e-5,
                                        window=window)
-    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
-        if window == 1 and k != "dv":
-            assert np.max(np.abs(ref[k])) == 0.0
-            log(f"  {k} max |got| {np.max(np.abs(g[k])):.3e}")
-            assert np.max(np.abs(g[k])) <= 1e-5, k
-            continue
-        st = _slice_stats(g[k], ref[k])
-        log(f"  {k} {st}")
-        assert _ok(st), (k, st)
-    _check_lambda_grads(g, ref)
+    check_gradients(g, ref, t, layer, dy, True, window)
 
 
 def test_bwd_v1_window_workload_slice(da):
@@ -259,8 +286,4 @@ def test_bwd_v1_window_workload_slice(da):
     ref = oracle.diff_attn_v1_backward(*(f64(t[k]) for k in ("q1", "q2", "k1", "k2", "v")),
                                        t["lambda"][layer], layer, f64(dy), True, 1e-5,
                                        window=window)
-    for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
-        st = _slice_stats(g[k], ref[k])
-        log(f"  {k} {st}")
-        assert _ok(st), (k, st)
-    _check_lambda_grads(g, ref)
+    check_gradients(g, ref, t, layer, dy, True, window)

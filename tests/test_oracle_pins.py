@@ -360,6 +360,33 @@ def test_sampled_rows_equal_full_rows():
     np.testing.assert_allclose(part[0, 0], full[0, 1, rows], rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 5)])
+def test_layer_sweep_equals_per_layer_v1(causal, window):
+    """The layer-sweep entry (branch outputs formed once, lambda applied per layer) equals the
+    plain V1 definition evaluated layer by layer, for every head, row and layer."""
+    rng = _rng(16)
+    q1, q2, k1, k2, v = _heads(rng, 2, 3, 37, 8, 16)
+    layers = [1, 2, 7, 32]
+    lams = np.array([rng.uniform(-0.6, 1.6, 3) for _ in layers])
+    inits = [oracle.lambda_init(l) for l in layers]
+    rows = [0, 3, 17, 36]
+    got = oracle.diff_attn_v1_layers(q1, q2, k1, k2, v, lams, inits, causal, 1e-5, rows=rows,
+                                     heads=[0, 2], window=window)
+    for li in range(len(layers)):
+        ref = oracle.diff_attn_v1(q1, q2, k1, k2, v, lams[li], inits[li], causal, 1e-5, rows=rows,
+                                  heads=[0, 2], window=window)
+        np.testing.assert_allclose(got[li], ref, rtol=0, atol=1e-12)
+    # a lambda taken from the wrong layer or head, or the wrong lambda_init, is visible
+    bad = oracle.diff_attn_v1_layers(q1, q2, k1, k2, v, lams[::-1], inits, causal, 1e-5, rows=rows,
+                                     heads=[0, 2], window=window)
+    assert np.max(np.abs(bad - got)) > 1e-3
+    bad = oracle.diff_attn_v1_layers(q1, q2, k1, k2, v, lams, inits[::-1], causal, 1e-5, rows=rows,
+                                     heads=[0, 2], window=window)
+    assert np.max(np.abs(bad - got)) > 1e-3
+    with pytest.raises(ValueError):
+        oracle.diff_attn_v1_layers(q1, q2, k1, k2, v, lams[:, :2], inits, causal)
+
+
 def test_row_blocking_does_not_change_values(monkeypatch):
     rng = _rng(15)
     q1, q2, k1, k2, v = (a[0, 0] for a in _heads(rng, 1, 1, 90, 16, 32))
