@@ -14,8 +14,9 @@ oracle to 1e-12.  Each gradient must therefore satisfy, per slice:
 * |kernel - model| / rms(oracle) <= BWD_MODEL_DIST everywhere: the kernel rounds where the model
   says, and what is left is fp32 summation order and the hardware exp2, which now and then put a
   value on the other side of a bf16 rounding boundary than the model does -- one bf16 step (at
-  most 2^-7 of the value) of one product term; measured up to 0.013 over the seeded cases, while
-  the max errors of kernel and model against the oracle agree to four decimals;
+  most 2^-7 of the value) of one product term, which is largest where few terms carry a sum
+  (peaked rows); measured up to 0.013 on N(0, 1) inputs and 0.020 on peaked ones, while the max
+  errors of kernel and model against the oracle agree to four decimals;
 * max |kernel - oracle| / rms(oracle) <= (the model's own max error) + BWD_MODEL_MARGIN;
 * that max <= BWD_MAX_TOL = 0.057 + 0.013, the model's worst case over the seeded cases plus the
   margin, and the RMS of the ratio <= BWD_RMS_TOL.
@@ -35,7 +36,7 @@ pytestmark = pytest.mark.gpu
 
 BWD_MAX_TOL = 7e-2
 BWD_RMS_TOL = 1e-2
-BWD_MODEL_DIST = 2e-2
+BWD_MODEL_DIST = 3e-2
 BWD_MODEL_MARGIN = 1e-2
 
 

@@ -8,7 +8,7 @@ import pytest
 import oracle
 import workloads as wl
 from oracle import compare
-from tests.helpers import bf16_ulps, dev, dev_lambda, f64, log, merge_stats, oracle_lambda, parallel_map
+from tests.helpers import beyond_output_rounding, dev, dev_lambda, f64, log, merge_stats, oracle_lambda, parallel_map
 
 pytestmark = pytest.mark.gpu
 
@@ -118,15 +118,14 @@ def test_decode_v1_workload_32k_every_sequence(da):
 
     def one(b):
         ref = _oracle(t, layer, batches=slice(b, b + 1))
-        return b, compare.bf16_stats(got[b:b + 1], ref), int(bf16_ulps(got[b:b + 1], ref).max())
+        return b, compare.bf16_stats(got[b:b + 1], ref), beyond_output_rounding(got[b:b + 1], ref)
 
     res = parallel_map(one, range(cfg["B"]))
     st = merge_stats([r[1] for r in res])
-    ulps = max(r[2] for r in res)
-    log(f"  {cfg['B']} sequences: {st}, largest distance from the correctly rounded result "
-        f"{ulps} bf16 step(s)")
+    excess = max(r[2] for r in res)
+    log(f"  {cfg['B']} sequences: {st}; largest error beyond the bf16 output rounding "
+        f"{excess:.2e} of the row RMS")
     assert compare.bf16_ok(st), st
-    # every step before the final bf16 rounding runs in fp32, so each element is the correctly
-    # rounded exact value or its neighbour (when the exact value lies within fp32 error of a
-    # rounding boundary)
-    assert ulps <= 1
+    # every step before the final bf16 store runs in fp32: past the store's own rounding, what is
+    # left is fp32 summation over the cache
+    assert excess <= 2e-3
