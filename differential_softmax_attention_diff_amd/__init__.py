@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
   diffattn_fwd_v2_workspace_bytes(B, Hkv, N, D)
   diffattn_decode(q1, q2, kcache, vcache, lq1, lk1, lq2, lk2, layer, ...)  V2 decode step
   diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits=0)
+  diffattn_decode_noalloc(q1, q2, kcache, vcache, lq1, ...)   V2 decode step without a workspace
+      (its partials use the library's fixed per-GPU scratch)
   diffattn_decode_paged(q1, q2, k_pages, v_pages, block_table, seq_lens, lq1, ...)  V2 decode,
       paged KV cache with per-sequence lengths
   diffattn_decode_v1(q1, q2, k1cache, k2cache, vcache, lq1, lk1, lq2, lk2, layer, ...)  V1 decode
@@ -30,7 +32,8 @@ import os
 __all__ = [
     "DiffAttnError", "load_library", "LIB_PATH",
     "DA_F32", "DA_BF16", "DA_V1_NO_NORM",
-    "diffattn_fwd_v1", "diffattn_fwd_v2", "diffattn_decode", "diffattn_decode_v1",
+    "diffattn_fwd_v1", "diffattn_fwd_v2", "diffattn_decode", "diffattn_decode_noalloc",
+    "diffattn_decode_v1", "DIFFATTN_DECODE_NOALLOC_MAX_BYTES",
     "diffattn_decode_paged", "diffattn_fwd_v1_train", "diffattn_bwd_v1",
     "diffattn_v1_train_stash_bytes", "diffattn_bwd_v1_workspace_bytes",
     "diffattn_fwd_v2_workspace_bytes", "diffattn_decode_workspace_bytes",
@@ -43,6 +46,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdiffattn
 DA_F32 = 0
 DA_BF16 = 1
 DA_V1_NO_NORM = 1
+DIFFATTN_DECODE_NOALLOC_MAX_BYTES = 16 << 20   # the fixed scratch of diffattn_decode_noalloc
 
 STATUS_NAMES = {0: "DA_OK", 1: "DA_ERR_NULL", 2: "DA_ERR_SHAPE", 3: "DA_ERR_UNSUPPORTED",
                 4: "DA_ERR_WORKSPACE", 5: "DA_ERR_HIP"}
@@ -99,6 +103,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.diffattn_decode_workspace_bytes.restype = sz
     lib.diffattn_decode.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp, sz, vp]
     lib.diffattn_decode.restype = i32
+    lib.diffattn_decode_noalloc.argtypes = [T, T, T, T, T, i32, i32, i32, i32, i32, i32, L, i32, vp]
+    lib.diffattn_decode_noalloc.restype = i32
     lib.diffattn_decode_paged.argtypes = [T, T, vp, vp, vp, vp, T, i32, i32, i32, i32, i32, i32, i32,
                                           i32, i32, L, i32, vp, sz, vp]
     lib.diffattn_decode_paged.restype = i32
@@ -334,6 +340,32 @@ def diffattn_decode(q1, q2, kcache, vcache, lq1=None, lk1=None, lq2=None, lk2=No
         _check(load_library().diffattn_decode(*descs, B, P, Hkv, L, D, dt, ctypes.byref(lam),
                                               int(num_splits), workspace.data_ptr(), ws_bytes, st),
                "diffattn_decode")
+    return out
+
+
+def diffattn_decode_noalloc(q1, q2, kcache, vcache, lq1=None, lk1=None, lq2=None, lk2=None,
+                            layer=1, *, out, num_splits=0, lambda_override=None, lambda_out=None,
+                            stream=None):
+    """``diffattn_decode`` without a workspace and without allocating: the caller passes ``out``
+    [B, P, D] (and every input); the split partials use the library's fixed per-GPU scratch of
+    DIFFATTN_DECODE_NOALLOC_MAX_BYTES.  Calls that overlap on one GPU share that scratch and must
+    be ordered."""
+    B, P, D = q1.shape
+    Hkv, L = kcache.shape[1], kcache.shape[2]
+    dt = _dtype_code(q1)
+    for nm, t in (("q2", q2), ("kcache", kcache), ("vcache", vcache), ("out", out)):
+        if t.dtype != q1.dtype:
+            raise TypeError(f"{nm} dtype {t.dtype} differs from q1 dtype {q1.dtype}")
+    descs = [_desc(q1, "q1", (B, P, D)), _desc(q2, "q2", (B, P, D)),
+             _desc(kcache, "kcache", (B, Hkv, L, D)), _desc(vcache, "vcache", (B, Hkv, L, D)),
+             _desc(out, "out", (B, P, D))]
+    lam = _lambda(lq1, lk1, lq2, lk2, layer, P, lambda_override, lambda_out, q1.device)
+    torch = _torch()
+    with torch.cuda.device(q1.device):
+        st = _stream(q1.device, stream)
+        _check(load_library().diffattn_decode_noalloc(*descs, B, P, Hkv, L, D, dt, ctypes.byref(lam),
+                                                      int(num_splits), st),
+               "diffattn_decode_noalloc")
     return out
 
 

@@ -247,12 +247,22 @@ size_t diffattn_decode_workspace_bytes(int32_t B, int32_t P, int32_t Hkv, int32_
   return (size_t)((int64_t)B * 2 * P * splits * (D + 2) * (int64_t)sizeof(float));
 }
 
-da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tensor vcache,
-                          da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t L, int32_t D,
-                          da_dtype dtype, const da_lambda* lam, int32_t num_splits,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of one V2 decode step (everything but the workspace); DA_OK with *empty set when the
+// call has nothing to do.
+da_status check_decode(const da_tensor& q1, const da_tensor& q2, const da_tensor& kcache,
+                       const da_tensor& vcache, const da_tensor& out, int32_t B, int32_t P,
+                       int32_t Hkv, int32_t L, int32_t D, da_dtype dtype, const da_lambda* lam,
+                       bool* empty) {
+  *empty = false;
   if (B < 0 || P < 0 || Hkv < 0 || L < 0) return DA_ERR_SHAPE;
-  if (B == 0 || P == 0) return DA_OK;
+  if (B == 0 || P == 0) {
+    *empty = true;
+    return DA_OK;
+  }
   if (L == 0 || Hkv == 0) return DA_ERR_SHAPE;  // the new token's own row is always present
   if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
   if (D != 128) return D <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
@@ -264,11 +274,14 @@ da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tenso
     const da_status s = check_tensor(*t, 2);
     if (s != DA_OK) return s;
   }
-  da_status s = check_lambda(lam, 256);
-  if (s != DA_OK) return s;
-  const size_t need = diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits);
-  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return DA_ERR_WORKSPACE;
+  return check_lambda(lam, 256);
+}
 
+// Launch one checked V2 decode step with its split partials in `workspace`.
+da_status run_decode(const da_tensor& q1, const da_tensor& q2, const da_tensor& kcache,
+                     const da_tensor& vcache, const da_tensor& out, int32_t B, int32_t P,
+                     int32_t Hkv, int32_t L, int32_t D, const da_lambda* lam, int32_t num_splits,
+                     void* workspace, void* stream) {
   da::DecodeParams p{};
   p.q1 = q1.ptr; p.q2 = q2.ptr; p.k = kcache.ptr; p.v = vcache.ptr; p.out = out.ptr;
   p.sq1 = strides(q1); p.sq2 = strides(q2); p.sk = strides(kcache); p.sv = strides(vcache);
@@ -282,6 +295,37 @@ da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tenso
   p.ws_ml = p.ws_acc + n_rows * D;
   p.lam = lambda_args(lam);
   return hip_status(da::launch_decode_v2(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tensor vcache,
+                          da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t L, int32_t D,
+                          da_dtype dtype, const da_lambda* lam, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  const da_status s = check_decode(q1, q2, kcache, vcache, out, B, P, Hkv, L, D, dtype, lam, &empty);
+  if (s != DA_OK || empty) return s;
+  const size_t need = diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return DA_ERR_WORKSPACE;
+  return run_decode(q1, q2, kcache, vcache, out, B, P, Hkv, L, D, lam, num_splits, workspace, stream);
+}
+
+da_status diffattn_decode_noalloc(da_tensor q1, da_tensor q2, da_tensor kcache, da_tensor vcache,
+                                  da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t L,
+                                  int32_t D, da_dtype dtype, const da_lambda* lam,
+                                  int32_t num_splits, void* stream) {
+  bool empty = false;
+  const da_status s = check_decode(q1, q2, kcache, vcache, out, B, P, Hkv, L, D, dtype, lam, &empty);
+  if (s != DA_OK || empty) return s;
+  const size_t need = diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits);
+  static_assert(da::kNoAllocScratchBytes == DIFFATTN_DECODE_NOALLOC_MAX_BYTES, "header constant");
+  if (need > da::kNoAllocScratchBytes) return DA_ERR_WORKSPACE;
+  void* scratch = da::noalloc_scratch();
+  if (scratch == nullptr) return DA_ERR_HIP;
+  return run_decode(q1, q2, kcache, vcache, out, B, P, Hkv, L, D, lam, num_splits, scratch, stream);
 }
 
 size_t diffattn_v1_train_stash_bytes(int32_t B, int32_t H, int32_t N, int32_t d) {

@@ -17,6 +17,8 @@
 //    it writes the split's (running max, running sum, un-normalised accumulator) per query head.
 //  * decode_combine: per (pair, batch) merges the splits of both heads by log-sum-exp, normalises,
 //    and stores out = O_2p - lambda_p O_2p+1 in bf16.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -315,6 +317,29 @@ hipError_t launch_step(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode_v2(const DecodeParams& p, hipStream_t stream) {
   return launch_step<false>(p, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Scratch of the allocation-free decode entry point: the split partials live in this fixed
+// device array instead of a caller workspace.  Each GPU the library runs on holds its own copy
+// (until the process ends).  In host code `scratch` names a host-side stand-in, not device
+// memory, so its device address is looked up once per device (with that device current) and
+// only that address is handed to the kernels.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    addr[dev] = ptr;
+  }
+  return addr[dev];
 }
 
 hipError_t launch_decode_v2_paged(const DecodeParams& p, hipStream_t stream) {

@@ -14,4 +14,10 @@ hipError_t launch_decode_v2(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_v2_paged(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_v1(const DecodeV1Params& p, hipStream_t stream);
 
+// The allocation-free decode's scratch: a fixed device array of kNoAllocScratchBytes per GPU.
+// Returns its device address on the current device (looked up on first use per device), or
+// nullptr if the lookup fails.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+void* noalloc_scratch();
+
 }  // namespace da

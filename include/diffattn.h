@@ -215,6 +215,27 @@ da_status diffattn_decode(da_tensor q1, da_tensor q2, da_tensor kcache, da_tenso
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * diffattn_decode_noalloc -- diffattn_decode for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, layouts, result and kernels as diffattn_decode, without the
+ * workspace: the split partials go to a fixed scratch array of DIFFATTN_DECODE_NOALLOC_MAX_BYTES
+ * (16 MiB) in device memory that the library holds on every GPU it runs on until the process
+ * ends.  The call allocates nothing (no hipMalloc, no allocating library routine).
+ *   - DA_ERR_WORKSPACE if diffattn_decode_workspace_bytes(B, P, Hkv, L, D, num_splits) exceeds
+ *     DIFFATTN_DECODE_NOALLOC_MAX_BYTES (e.g. B = 64, 32 query heads, the default 8 splits at
+ *     L = 32768 need 8.5 MB: fits); nothing is enqueued then.
+ *   - DA_ERR_HIP if the scratch's device address cannot be found on the current device.
+ *   - Every call on one GPU uses that GPU's one scratch array, and nothing in it needs clearing
+ *     (each call writes every partial it reads): calls that overlap on one GPU (several streams
+ *     or threads at once) race and must be ordered by the caller.
+ */
+#define DIFFATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+da_status diffattn_decode_noalloc(da_tensor q1, da_tensor q2, da_tensor kcache, da_tensor vcache,
+                                  da_tensor out, int32_t B, int32_t P, int32_t Hkv, int32_t L,
+                                  int32_t D, da_dtype dtype, const da_lambda* lam,
+                                  int32_t num_splits, void* stream);
+
+/*
  * diffattn_decode_paged -- the V2 decode step on the serving layout: a pool of KV pages addressed
  * through a per-sequence block table, each sequence with its own length (the layout of the
  * production inference servers that ai-engineering.academy "Atención Diferencial (V2)", section

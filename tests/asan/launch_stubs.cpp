@@ -12,5 +12,6 @@ hipError_t launch_v2_bf16(const PrefillParams&, hipStream_t) { return hipErrorNo
 hipError_t launch_decode_v2(const DecodeParams&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_decode_v2_paged(const DecodeParams&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_decode_v1(const DecodeV1Params&, hipStream_t) { return hipErrorNotSupported; }
+void* noalloc_scratch() { return nullptr; }
 
 }  // namespace da

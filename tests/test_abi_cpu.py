@@ -41,7 +41,7 @@ def _declared_functions():
 
 def test_header_symbols_exported(da):
     names = _declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     lib = ctypes.CDLL(da.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -133,6 +133,31 @@ def test_v2_and_decode_host_validation(da):
     assert dec(0x30000, need, P=3) == 2
     assert dec(0x30000, need, P=16, Hkv=1) == 3              # 32 query heads on one KV head
     assert dec(0x30000, need, L=0) == 2
+
+
+def test_decode_noalloc_host_validation(da):
+    """The allocation-free decode checks its arguments like diffattn_decode and refuses sizes
+    beyond its fixed scratch on the host, before any HIP call (so this runs without a GPU)."""
+    lib = da.load_library()
+    t5 = [_t() for _ in range(5)]
+    lam = _lam(dl=128)
+    call = lambda B=2, P=4, Hkv=2, L=1000, D=128, dt=1, splits=0, lamp=ctypes.byref(lam): \
+        lib.diffattn_decode_noalloc(*t5, B, P, Hkv, L, D, dt, lamp, splits, None)
+    assert call(B=0) == 0
+    assert call(P=3) == 2
+    assert call(D=64) == 3
+    assert call(dt=0) == 3
+    assert call(L=0) == 2
+    assert call(P=16, Hkv=1) == 3
+    assert call(lamp=None) == 1
+    bad = list(t5)
+    bad[4] = _t(ptr=0x10008)
+    assert lib.diffattn_decode_noalloc(*bad, 2, 4, 2, 1000, 128, 1, ctypes.byref(lam), 0, None) == 1
+    # 64 x 32 query heads x 16 splits x 130 floats is 17 MB, beyond the 16 MiB scratch
+    assert da.diffattn_decode_workspace_bytes(64, 16, 8, 8192, 128, 16) > da.DIFFATTN_DECODE_NOALLOC_MAX_BYTES
+    assert call(B=64, P=16, Hkv=8, L=8192, splits=16) == 4
+    # the decode workload's own partials fit
+    assert da.diffattn_decode_workspace_bytes(64, 16, 8, 32768, 128, 0) <= da.DIFFATTN_DECODE_NOALLOC_MAX_BYTES
 
 
 def test_v2_workspace_size_formula(da):
