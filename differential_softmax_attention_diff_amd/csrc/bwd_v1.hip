@@ -136,15 +136,17 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------------------------
 // dK_1, dK_2, dV: per 64 keys of a head, 16 per wave, both branches in each wave
 // LDS layouts of the dK/dV kernel's tiles, each read both row by row (16x16x32 MFMA A operand:
-// 16 rows at one 16-byte chunk per 16-lane phase) and transposed (ds_read_b64_tr_b16: 8 rows of
-// 32 bytes per 32-lane phase).  The 16-byte chunk index is XORed with a function of the row that
-// is a bijection on the rows of a row-wise phase and keeps the transposed rows' 32-byte pairs
-// apart, so both patterns are free of bank conflicts on 64 banks of 4 bytes.
-__device__ __forceinline__ int q16_swz(int row) { return (((row >> 1) & 3) << 1) | ((row >> 3) & 1); }
+// lane n of each 16-lane group takes row n, the group index picks the 16-byte chunk) and
+// transposed (ds_read_b64_tr_b16: 8 rows of 32 bytes per 32-lane half).  The 16-byte chunk index
+// is XORed with the row's low three bits (Q tiles, 8 chunks per row) or with twice them (dO,
+// 16 chunks per row).  Both read patterns of both tiles then measure free of bank conflicts
+// (SQ_LDS_BANK_CONFLICT = 0 on gfx950, in an access-pattern probe); the earlier choices, which
+// also folded row bit 3 into the chunk index, were 2-way conflicted on the row-wise reads.
+__device__ __forceinline__ int q16_swz(int row) { return row & 7; }
 __device__ __forceinline__ int q16_off(int row, int col) {
   return row * kD + ((((col >> 3) ^ q16_swz(row))) << 3) + (col & 7);
 }
-__device__ __forceinline__ int o16_swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int o16_swz(int row) { return (row & 7) << 1; }
 __device__ __forceinline__ int o16_off(int row, int col) {
   return row * kDV + ((((col >> 3) ^ o16_swz(row))) << 3) + (col & 7);
 }
@@ -393,6 +395,19 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
 
 // ---------------------------------------------------------------------------------------------
 // dQ_1, dQ_2: per 128 query rows, 32 per wave, both branches in each wave
+// LDS layout of the dQ kernel's K tiles (32 rows x 64 columns), read row by row (lane c = lane %
+// 32 takes row c, lane / 32 the 16-byte chunk) and transposed (ds_read_b64_tr_b16, four 4-row
+// groups of 16-byte runs per 32-lane half).  The chunk index is XORed with a linear function of
+// row bits 1-3 (6 r1 ^ 2 r2 ^ 3 r3) that keeps both patterns free of bank conflicts (measured
+// SQ_LDS_BANK_CONFLICT = 0 in an access-pattern probe; the forward's (row >> 1) & 7 layout is
+// 2-way conflicted on these transposed reads).
+__device__ __forceinline__ int kq_swz(int row) {
+  return (((row >> 1) & 1) * 6) ^ (((row >> 2) & 1) * 2) ^ (((row >> 3) & 1) * 3);
+}
+__device__ __forceinline__ int kq_off(int row, int col) {
+  return row * kD + ((((col >> 3) ^ kq_swz(row))) << 3) + (col & 7);
+}
+
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   constexpr int KT = kT * kD;                  // one K tile
   constexpr int STAGE = 2 * KT + kT * kDV;     // K_1 | K_2 | V
@@ -458,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   {
     const int e = 512 * w + 8 * lane;
     k_lrow = e / kD;
-    k_lchunk = (uint32_t)((((e % kD) >> 3) ^ k_swz<kD>(k_lrow)) * 16);
+    k_lchunk = (uint32_t)((((e % kD) >> 3) ^ kq_swz(k_lrow)) * 16);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int ev = 512 * (w + 4 * i) + 8 * lane;
@@ -485,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dq1[i][r] = 0.f; dq2[i][r] = 0.f; }
 
-  const int k_rd = k_off<kD>(c, 8 * hh);
+  const int k_rd = kq_off(c, 8 * hh);
   // the V tile is only read row by row here, so it takes the 128-column K-tile layout, whose
   // row-wise reads are free of bank conflicts
   const int v_rd = k_off<kDV>(c, 8 * hh);
@@ -536,12 +551,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
       const bf16x8 sb2 = cvt8_sum(s2, 8 * u, dummy);
 #pragma unroll
       for (int dbk = 0; dbk < 2; ++dbk) {
-        const u32x2 lo1 = lds_read_tr(st + k_off<kD>(16 * u + trow, 32 * dbk + tcol));
-        const u32x2 hi1 = lds_read_tr(st + k_off<kD>(16 * u + 8 + trow, 32 * dbk + tcol));
+        const u32x2 lo1 = lds_read_tr(st + kq_off(16 * u + trow, 32 * dbk + tcol));
+        const u32x2 hi1 = lds_read_tr(st + kq_off(16 * u + 8 + trow, 32 * dbk + tcol));
         const u32x4 a1 = {lo1[0], lo1[1], hi1[0], hi1[1]};
         dq1[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), sb1, dq1[dbk], 0, 0, 0);
-        const u32x2 lo2 = lds_read_tr(st + KT + k_off<kD>(16 * u + trow, 32 * dbk + tcol));
-        const u32x2 hi2 = lds_read_tr(st + KT + k_off<kD>(16 * u + 8 + trow, 32 * dbk + tcol));
+        const u32x2 lo2 = lds_read_tr(st + KT + kq_off(16 * u + trow, 32 * dbk + tcol));
+        const u32x2 hi2 = lds_read_tr(st + KT + kq_off(16 * u + 8 + trow, 32 * dbk + tcol));
         const u32x4 a2 = {lo2[0], lo2[1], hi2[0], hi2[1]};
         dq2[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a2), sb2, dq2[dbk], 0, 0, 0);
       }
