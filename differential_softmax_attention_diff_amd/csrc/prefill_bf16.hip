@@ -192,6 +192,7 @@ void prefill_kernel(const PrefillParams p) {
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   float mrun = kNegBig, lrun = 0.f;
   const float sl2 = p.scale_log2;
+  float nmrun = -mrun * sl2;  // -m log2(e)/sqrt(d), updated whenever m moves
 
   // Per-lane LDS byte addresses of the MFMA operands, one register each; they flip to the other
   // buffer after use (one XOR).  Both swizzles act on address bits that the operand index only
@@ -245,7 +246,7 @@ void prefill_kernel(const PrefillParams p) {
   // P operands (16 keys each); tl gets the lane's sum of the rounded weights
   // (s is overwritten by the weights; the rare slow path forms the scores again from LDS)
   auto weights = [&](f32x16& e, bf16x8& p0, bf16x8& p1, float& tl) {
-    const float nm = -mrun * sl2;
+    const float nm = nmrun;
 #pragma unroll
     for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(e[r], sl2, nm));
     tl = 0.f;
@@ -276,6 +277,7 @@ void prefill_kernel(const PrefillParams p) {
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
       mrun = fmaxf(mrun, pmax(mx));
+      nmrun = -mrun * sl2;
     }
     bf16x8 p0, p1;
     float tl;
@@ -293,6 +295,7 @@ void prefill_kernel(const PrefillParams p) {
       const float mnew = fmaxf(mrun, mx);
       const float alpha = exp2f((mrun - mnew) * sl2);
       mrun = mnew;
+      nmrun = -mrun * sl2;
       lrun *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[db] *= alpha;
