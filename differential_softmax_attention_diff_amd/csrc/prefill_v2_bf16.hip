@@ -206,6 +206,7 @@ void prefill_v2_kernel(const PrefillParams p) {
   for (int t = 0; t < 8; ++t) { acca[t] = f32x4{0.f, 0.f, 0.f, 0.f}; accb[t] = f32x4{0.f, 0.f, 0.f, 0.f}; }
   float ma = kNegBig, mb = kNegBig, la = 0.f, lb = 0.f;
   const float sl2 = p.scale_log2;
+  float nma = -ma * sl2, nmb = -mb * sl2;  // -m log2(e)/sqrt(D) per head, formed when m moves
 
   auto k_op = [&](uint32_t kb, int h, int ks) {
     return *reinterpret_cast<const bf16x8*>(sb + ((kb ^ (64u * ks)) + 4096u * h));
@@ -246,9 +247,9 @@ void prefill_v2_kernel(const PrefillParams p) {
   };
   // weights exp2((s - m) log2(e) / sqrt(D)) against the reference max m, packed as k-slot
   // 4 h + r (fp16, or bf16 on the bf16 path); tl gets the lane's sum of the rounded weights
-  auto weights = [&](const f32x4 (&s)[2], float m, float& tl, auto half_tag) {
+  // nm: -m log2(e)/sqrt(D) for the head's reference max m, formed when m moves
+  auto weights = [&](const f32x4 (&s)[2], float nm, float& tl, auto half_tag) {
     constexpr bool kHalf = decltype(half_tag)::value;
-    const float nm = -m * sl2;
     u32x4 o;
     tl = 0.f;
 #pragma unroll
@@ -286,7 +287,7 @@ void prefill_v2_kernel(const PrefillParams p) {
     l *= alpha;
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] *= alpha;
-    return weights(s, m, tl, half_tag);
+    return weights(s, -m * sl2, tl, half_tag);
   };
   // One tile, both heads: scores, weights (moving a head's m when some weight would exceed
   // 2^12), then O^T += V^T P^T with each V^T operand feeding both heads' MFMAs.  kSlow: the bf16
@@ -313,14 +314,22 @@ void prefill_v2_kernel(const PrefillParams p) {
       };
       ma = fmaxf(ma, row4_max(tile_max(sa)));
       mb = fmaxf(mb, row4_max(tile_max(sbb)));
+      nma = -ma * sl2;
+      nmb = -mb * sl2;
     }
     using HT = std::integral_constant<bool, !kSlow>;
     float tla, tlb;
-    u32x4 pa = weights(sa, ma, tla, HT{});
-    if (!kFirst && __any(!(tla <= kCapSum))) pa = move_max(kb, qa, kt, masked, ma, la, acca, tla, HT{});
+    u32x4 pa = weights(sa, nma, tla, HT{});
+    if (!kFirst && __any(!(tla <= kCapSum))) {
+      pa = move_max(kb, qa, kt, masked, ma, la, acca, tla, HT{});
+      nma = -ma * sl2;
+    }
     la += tla;
-    u32x4 pb = weights(sbb, mb, tlb, HT{});
-    if (!kFirst && __any(!(tlb <= kCapSum))) pb = move_max(kb, qb, kt, masked, mb, lb, accb, tlb, HT{});
+    u32x4 pb = weights(sbb, nmb, tlb, HT{});
+    if (!kFirst && __any(!(tlb <= kCapSum))) {
+      pb = move_max(kb, qb, kt, masked, mb, lb, accb, tlb, HT{});
+      nmb = -mb * sl2;
+    }
     lb += tlb;
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
