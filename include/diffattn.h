@@ -25,10 +25,13 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
  *    The library never synchronises; a result is valid once the stream has reached it.
  *  - All argument checks run on the host before anything is enqueued.  On any error nothing
- *    is launched and no output byte is written.  Empty problems (B == 0 or N/L == 0) return
- *    DA_OK and enqueue nothing.  No entry point aborts, throws or prints.
- *  - The library keeps no mutable global state; concurrent calls on different streams are
- *    safe as long as their output/workspace buffers do not overlap.
+ *    is launched and no output byte is written.  Empty problems (a zero batch, head or pair
+ *    count, or N == 0 in a prefill) return DA_OK and enqueue nothing, before any pointer is
+ *    looked at.  A decode step with L == 0 is DA_ERR_SHAPE: its cache holds at least the new
+ *    token.  No entry point aborts, throws or prints.
+ *  - Apart from the one scratch array of diffattn_decode_noalloc, the library keeps no
+ *    mutable global state; concurrent calls on different streams are safe as long as their
+ *    output/workspace buffers do not overlap.
  *  - Causal masking: query row i sees key j iff j <= i (square problem, N queries, N keys).
  */
 #ifndef DIFFATTN_H
