@@ -196,7 +196,8 @@ BENCH_HEADS = (0, 5, 15)
 def test_bwd_v1_bench_launch(da, window):
     """The backward as the benchmark times it: the 4K workload's inputs (B=4 H=16 N=4096; with the
     1024-key window, the sliding-window workload's), its upstream gradient (seed 77, float32
-    draws) and one launch over all 64 (batch, head) slices.  Every gradient of all four batches of
+    draws) and one launch over all 64 (batch, head) slices, after the training forward whose output
+    must equal the plain forward's bit for bit.  Every gradient of all four batches of
     heads 0, 5 and 15 is checked against the oracle and the rounding model; a head's lambda-vector
     gradients sum over its four batches, so they are checked whole.  At this shape the rounding
     model itself reaches more than the seeded cases' 0.057 (0.086 on dQ_1 of head 5 under the
@@ -211,7 +212,13 @@ def test_bwd_v1_bench_launch(da, window):
     assert cfg.get("window", 0) == window
     dy = wl.f32_to_bf16_bits(np.random.default_rng(77).standard_normal((B, H, N, 2 * d), dtype=np.float32))
     log(f"bwd v1 bench launch B={B} H={H} N={N} window={window} layer={layer}")
-    _, g = _run(da, t, layer, True, dy, window=window)
+    out, g = _run(da, t, layer, True, dy, window=window)
+    # the training forward's output equals the plain forward's bit for bit (the latter is checked
+    # on every row of this launch in the forward tests), so the training step is covered whole
+    fwd = da.diffattn_fwd_v1(*(dev(t[k]) for k in ("q1", "q2", "k1", "k2", "v")),
+                             *dev_lambda(t["lambda"][layer]), layer=layer, window=window)
+    assert np.array_equal(out, fwd.float().cpu().numpy())
+    del fwd
 
     def head(h):
         th = {k: np.ascontiguousarray(t[k][:, h:h + 1]) for k in ("q1", "q2", "k1", "k2", "v")}
