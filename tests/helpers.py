@@ -62,7 +62,7 @@ def parallel_map(fn, items, threads=None):
 
 
 def merge_stats(stats):
-    """One bf16 verdict over several compared pieces of an output: the max error over all of them
+    """One bf16 decision over several compared pieces of an output: the max error over all of them
     and the share of within-bound elements over all their elements together (the bar applies to
     the output tensor; a piece of a few thousand elements is too small a sample for 99.9 %)."""
     n = sum(s["n"] for s in stats)

@@ -1,6 +1,6 @@
 """Pins of the parity metrics in ``oracle/compare.py`` on hand-computed arrays (CPU).
 
-Every GPU parity verdict goes through ``row_rel_error``, ``normalise_by_ref_rms``, ``bf16_stats``
+Every GPU parity decision goes through ``row_rel_error``, ``normalise_by_ref_rms``, ``bf16_stats``
 and ``bf16_ok``, so a slip there would loosen every GPU test at once.  The checks below fix each
 function on arrays whose answer is worked out by hand:
 
