@@ -534,7 +534,7 @@ def cpu_baseline(cfg, t, budget_s):
 
 
 def cpu_baseline_long(cfg, t, budget_s):
-    """The float64 oracle on seeded query rows of the 128K workload (layer 1): 4 blocks of 64
+    """The float64 oracle on seeded query rows of the 128K workload (layer 1): up to 8 blocks of 64
     uniform rows per head, head after head, until ~budget_s of oracle time have passed (the bf16
     to float64 conversion of a head's inputs, done once per head, is not timed).  Row i of a
     causal head costs 8*d*(i+1) algorithmic flops (two score rows of i+1 keys, one weighted sum
@@ -552,7 +552,7 @@ def cpu_baseline_long(cfg, t, budget_s):
     for h in range(cfg["H"]):
         sl = [f32(t[k][0:1, h:h + 1]) for k in ("q1", "q2", "k1", "k2", "v")]
         heads += 1
-        for _ in range(4):
+        for _ in range(8):
             rows = np.sort(rng.choice(N, size=64, replace=False))
             t0 = time.perf_counter()
             oracle.diff_attn_v1(*sl, lam[h:h + 1], lam_init, True, cfg["eps"], rows=rows)
