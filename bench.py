@@ -28,10 +28,9 @@ FLOP and byte conventions (per launch):
   V1 backward algorithmic flops  = B*H * 16*d * Np   (dO V^T, dV, and dQ_b, dK_b per branch)
               executed MFMA flops = B*H * 28*d * Np  (scores and dO V^T formed in both kernels)
 with Np = N(N+1)/2 causal query-key pairs (the window's visible pairs for the sliding window).
-MFMA-bound lines whose shader clock was sampled also carry roofline.executed_frac_at_sampled_clock:
-the executed fraction of the dense peak scaled to that clock (the peak assumes 2.4 GHz; under
-sustained MFMA load the part runs power-limited below it).  Short timed regions give few samples
-(timing.shader_clock_samples).
+timing.shader_clock_mhz_median is the AMD SMI GFX clock reading sampled during the timed steps:
+indicative only (the effective clock, counted cycles over kernel time, is what the rocprofv3
+counter summaries give); short timed regions give few samples (timing.shader_clock_samples).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
        [--only long|v1|v2|decode|decode_v1|swa|paged|bwd|bwd_swa|train]
@@ -58,7 +57,6 @@ import workloads as wl  # noqa: E402
 METRIC = "diff-attn fwd TFLOP/s (% bf16 MFMA peak); decode HBM GB/s (% of 8 TB/s)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-PEAK_CLOCK_MHZ = 2400.0     # the shader clock behind the dense MFMA peak (256 CUs)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", "prefill_bf16.hip"),
@@ -573,15 +571,6 @@ def cpu_baseline_long(cfg, t, budget_s):
 
 # ------------------------------------------------------------------------------------------------
 
-def clock_adjusted(res):
-    """For an MFMA-bound line whose shader clock was sampled: the executed-flop fraction of the
-    peak the chip can issue at that clock (the dense peak scales with the clock; under sustained
-    MFMA load the part runs power-limited below the 2.4 GHz behind the nominal figure)."""
-    rl, clk = res.get("roofline", {}), res.get("timing", {}).get("shader_clock_mhz_median")
-    if rl.get("bound") == "mfma" and rl.get("executed_mfma_frac") is not None and clk:
-        rl["executed_frac_at_sampled_clock"] = round(rl["executed_mfma_frac"] * PEAK_CLOCK_MHZ / clk, 4)
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -668,8 +657,6 @@ def main():
         torch.cuda.empty_cache()
     if head is None:
         head = secondary.pop(0)
-    for res in [head] + secondary:
-        clock_adjusted(res)
 
     line = {
         "metric": METRIC,
