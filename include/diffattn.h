@@ -23,7 +23,9 @@
  *  - The caller owns every buffer.  The library allocates no device or host memory; the
  *    decode path writes its split partials into a caller-provided device workspace.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
- *    The library never synchronises; a result is valid once the stream has reached it.
+ *    The library never synchronises; a result is valid once the stream has reached it.  Calls
+ *    enqueue kernels only (no allocation, memset or copy), so they can be captured in a HIP
+ *    graph and replayed with new contents in the same buffers.
  *  - All argument checks run on the host before anything is enqueued.  On any error nothing
  *    is launched and no output byte is written.  Empty problems (a zero batch, head or pair
  *    count, or N == 0 in a prefill) return DA_OK and enqueue nothing, before any pointer is
