@@ -372,7 +372,7 @@ def bench_decode_paged(da, torch, steps, warmup):
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic("v2_decode_paged", "decode"),
                      "algorithmic_bytes": nbytes,
-                     "kernel": "decode_partial_kernel<4,true> + decode_combine_kernel (whole step)"},
+                     "kernel": "decode_paged_balanced_kernel<4> + decode_combine_kernel (whole step)"},
     }
 
 

@@ -15,8 +15,13 @@
 //      - P.V on the vector ALUs: 16 lanes cover one 256-byte V row (8 channels each) and read the
 //        G weights of that key as an LDS broadcast;
 //    it writes the split's (running max, running sum, un-normalised accumulator) per query head.
+//  * decode_paged_balanced: the paged cache's sequences have their own lengths, so instead of
+//    splitting each sequence, the blocks of all sequences are dealt in equal contiguous runs to as
+//    many workgroups per KV head as the chip holds at once; a run covers pieces of one or more
+//    sequences, each processed as above and written as its own partial.
 //  * decode_combine: per (pair, batch) merges the splits of both heads by log-sum-exp, normalises,
 //    and stores out = O_2p - lambda_p O_2p+1 in bf16.
+#include <algorithm>
 #include <mutex>
 
 #include "device_common.hpp"
@@ -29,38 +34,47 @@ constexpr int kD = 128;
 constexpr int kKB = 256;  // keys per block (64 per wavefront)
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;
+constexpr int kPagedRounds = 1;  // balanced paged pass: workgroups per resident slot
 
 // G = query heads per KV head (2P / Hkv): 2, 4, 8 or 16.  PAGED: the cache is a pool of pages
 // [num_pages, Hkv, page_size, D] addressed through a per-sequence block table, and every sequence
 // has its own length (the serving layout); otherwise [B, Hkv, L, D] with strides and one length.
 template <int G, bool PAGED>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
+struct PartialLds {
+  float sc[G][kKB];                             // scores of the block, per head
+  __attribute__((aligned(16))) float pw[kKB][G];  // exp-weights, per key
+  float alpha[G];
+  float red[4][G][kD];
+  int tab[PAGED ? 2 : 1][PAGED ? kKB : 1];      // page of each page-sized run of a block
+};
+
+// keys of paged sequence b: its length clamped to [0, L] and to the table's extent
+__device__ __forceinline__ int paged_len(const DecodeParams& p, int b) {
+  return (int)min((int64_t)max(p.seq_lens[b], 0), min((int64_t)p.L, (int64_t)p.max_blocks << p.page_shift));
+}
+__device__ __forceinline__ int n_blocks(int keys) { return (keys + kKB - 1) / kKB; }
+
+// One piece of the cache of sequence b and KV head g: keys [k_begin, k_end) (k_begin a multiple
+// of the block size) in blocks of 256.  Each query head hq of the KV head gets its (running max,
+// running sum, un-normalised accumulator) at workspace row hq * ws_stride + ws_off.  Every thread
+// of the workgroup calls it with the same arguments; it ends on a barrier, so that it can be
+// called again for another piece.
+template <int G, bool PAGED>
+__device__ __forceinline__ void partial_range(const DecodeParams& p, PartialLds<G, PAGED>& sm, int b,
+                                              int g, int k_begin, int k_end, int64_t ws_stride,
+                                              int64_t ws_off) {
   constexpr int SLOTS = (G + 3) / 4;  // heads whose softmax state one wavefront owns
-  __shared__ float sc_lds[G][kKB];    // scores of the block, per head
-  __shared__ __attribute__((aligned(16))) float pw_lds[kKB][G];  // exp-weights, per key
-  __shared__ float alpha_lds[G];
-  __shared__ float red_lds[4][G][kD];
-  __shared__ int tab_lds[PAGED ? 2 : 1][PAGED ? kKB : 1];  // page of each page-sized run of a block
+  auto& sc_lds = sm.sc;
+  auto& pw_lds = sm.pw;
+  auto& alpha_lds = sm.alpha;
+  auto& red_lds = sm.red;
+  auto& tab_lds = sm.tab;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
   const int l16 = lane & 15;
   const int grp = lane >> 4;
-
-  // keys of this sequence (paged: its own length, clamped to the table's extent)
-  const int seq_len =
-      PAGED ? (int)min((int64_t)max(p.seq_lens[b], 0), min((int64_t)p.L, (int64_t)p.max_blocks << p.page_shift))
-            : p.L;
-  // the sequence's 256-key blocks are dealt evenly to the splits, so that with per-sequence
-  // lengths every split of a sequence gets the same share (empty only when it has fewer blocks
-  // than splits)
-  const int nblk = (seq_len + kKB - 1) / kKB;
-  const int k_begin = (int)(((int64_t)split * nblk) / p.splits) * kKB;
-  const int k_end = min(seq_len, (int)(((int64_t)(split + 1) * nblk) / p.splits) * kKB);
   const float c2 = p.scale_log2;
 
   const bf16* kbase = static_cast<const bf16*>(p.k) + b * p.sk.sb + g * p.sk.sh;
@@ -240,14 +254,13 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
 #pragma unroll
       for (int e = 0; e < 8; ++e) red_lds[w][h][8 * l16 + e] = acc[h][e];
   }
-  // softmax statistics of the split
-  const int two_p = 2 * p.P;
+  // softmax statistics of the piece
 #pragma unroll
   for (int j = 0; j < SLOTS; ++j) {
     const int h = w + 4 * j;
     if (h < G && lane == 0) {
       const int hq = g * G + h;
-      float* ml = p.ws_ml + (((int64_t)b * two_p + hq) * p.splits + split) * 2;
+      float* ml = p.ws_ml + ((int64_t)hq * ws_stride + ws_off) * 2;
       ml[0] = mrun[j];
       ml[1] = lrun[j];
     }
@@ -258,11 +271,99 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodePa
     const int ch = idx % kD;
     const float s = red_lds[0][h][ch] + red_lds[1][h][ch] + red_lds[2][h][ch] + red_lds[3][h][ch];
     const int hq = g * G + h;
-    p.ws_acc[(((int64_t)b * two_p + hq) * p.splits + split) * kD + ch] = s;
+    p.ws_acc[((int64_t)hq * ws_stride + ws_off) * kD + ch] = s;
+  }
+  __syncthreads();  // the LDS is free for the next piece
+}
+
+// Per-sequence splits: workgroup (split, g, b) takes an equal share of sequence b's blocks.
+template <int G, bool PAGED>
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const DecodeParams p) {
+  __shared__ PartialLds<G, PAGED> sm;
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int seq_len = PAGED ? paged_len(p, b) : p.L;
+  // the sequence's 256-key blocks are dealt evenly to the splits, so that with per-sequence
+  // lengths every split of a sequence gets the same share (empty only when it has fewer blocks
+  // than splits)
+  const int nblk = n_blocks(seq_len);
+  const int k_begin = (int)(((int64_t)split * nblk) / p.splits) * kKB;
+  const int k_end = min(seq_len, (int)(((int64_t)(split + 1) * nblk) / p.splits) * kKB);
+  partial_range<G, PAGED>(p, sm, b, g, k_begin, k_end, p.splits, (int64_t)b * 2 * p.P * p.splits + split);
+}
+
+// inclusive prefix sum over the wavefront
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Paged cache, balanced over uneven lengths: the blocks of all sequences, taken in sequence
+// order (TB in all), are dealt to the NW = gridDim.x workgroups of a KV head in equal contiguous
+// runs; workgroup w takes global blocks [w TB / NW, (w + 1) TB / NW).  A run may start or end
+// inside a sequence and may cover several; each (workgroup w, sequence b) piece writes its
+// partial at slot w + b of the query head's NW + B slots.  Slots are unique: along the runs both
+// w and b only grow, and each step moves at least one of them.
+template <int G>
+__global__ __launch_bounds__(kThreads) void decode_paged_balanced_kernel(const DecodeParams p) {
+  __shared__ PartialLds<G, true> sm;
+  __shared__ int64_t red64[kThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int wg = blockIdx.x;
+  const int g = blockIdx.y;
+  const int64_t nw = gridDim.x;
+  int64_t part = 0;
+  for (int b = tid; b < p.B; b += kThreads) part += n_blocks(paged_len(p, b));
+  part = wave_sum64(part);
+  if (lane == 0) red64[wv] = part;
+  __syncthreads();
+  int64_t tb = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) tb += red64[i];
+  const int64_t x0 = wg * tb / nw;
+  const int64_t x1 = (wg + 1) * tb / nw;
+  if (x0 >= x1) return;  // the same for every thread
+  // first sequence of the run: the first b whose blocks end past x0 (each wavefront finds it)
+  int64_t base = 0;  // global index of sequence b's first block
+  int b = p.B;
+  for (int c = 0; c < p.B; c += 64) {
+    const int bb = c + lane;
+    const int64_t n = bb < p.B ? n_blocks(paged_len(p, bb)) : 0;
+    const int64_t incl = wave_incl_scan(n, lane);
+    const uint64_t hit = __ballot(base + incl > x0);
+    if (hit != 0) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      b = c + l;
+      base += __shfl(incl - n, l);
+      break;
+    }
+    base += __shfl(incl, 63);
+  }
+  for (; b < p.B && base < x1; ++b) {
+    const int len = paged_len(p, b);
+    const int nb = n_blocks(len);
+    const int64_t lo = max(x0, base) - base;
+    const int64_t hi = min(x1, base + nb) - base;
+    if (lo < hi)
+      partial_range<G, true>(p, sm, b, g, (int)lo * kKB, min(len, (int)hi * kKB), nw + p.B, wg + b);
+    base += nb;
   }
 }
 
 __global__ __launch_bounds__(kD) void decode_combine_kernel(const DecodeParams p) {
+  __shared__ int64_t red64[2][kD / 64];
   const int pair = blockIdx.x;
   const int b = blockIdx.y;
   const int ch = threadIdx.x;
@@ -270,19 +371,56 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(const DecodeParams p
   const float lam = head_lambda(p.lam, pair, lane);
   if (p.lam.out != nullptr && b == 0 && ch == 0) p.lam.out[pair] = lam;
   const int two_p = 2 * p.P;
+  // this sequence's partials: rows hq * stride + first .. + last of the query head hq
+  int64_t stride = p.splits, first = (int64_t)b * two_p * p.splits, last = first + p.splits - 1;
+  int64_t tot_blocks = 0;
+  if (p.stream_wgs > 0) {
+    // the balanced paged pass: the workgroups whose runs of blocks meet this sequence's
+    int64_t tot = 0, pre = 0;
+    for (int i = ch; i < p.B; i += kD) {
+      const int64_t n = n_blocks(paged_len(p, i));
+      tot += n;
+      if (i < b) pre += n;
+    }
+    tot = wave_sum64(tot);
+    pre = wave_sum64(pre);
+    if (lane == 0) {
+      red64[0][ch >> 6] = tot;
+      red64[1][ch >> 6] = pre;
+    }
+    __syncthreads();
+    tot = red64[0][0] + red64[0][1];
+    pre = red64[1][0] + red64[1][1];
+    const int64_t nw = p.stream_wgs;
+    const int64_t nb = n_blocks(paged_len(p, b));
+    // the workgroup whose run [w tot / nw, (w + 1) tot / nw) holds global block x
+    auto owner = [&](int64_t x) { return ((x + 1) * nw + tot - 1) / tot - 1; };
+    stride = nw + p.B;
+    first = nb > 0 ? owner(pre) + b : 0;
+    last = nb > 0 ? owner(pre + nb - 1) + b : -1;
+    tot_blocks = tot;
+  }
+  // with more workgroups than blocks some runs are empty, and their slots hold nothing
+  auto skip = [&](int64_t s) {
+    if (p.stream_wgs == 0) return false;
+    const int64_t w = s - b;
+    return w * tot_blocks / p.stream_wgs == (w + 1) * tot_blocks / p.stream_wgs;
+  };
   float o[2];
 #pragma unroll
   for (int br = 0; br < 2; ++br) {
     const int hq = 2 * pair + br;
-    const float* ml = p.ws_ml + ((int64_t)b * two_p + hq) * p.splits * 2;
-    const float* ac = p.ws_acc + ((int64_t)b * two_p + hq) * p.splits * kD;
+    const float* ml = p.ws_ml + (hq * stride) * 2;
+    const float* ac = p.ws_acc + (hq * stride) * kD;
     float m = kNegBig;
-    for (int s = 0; s < p.splits; ++s) m = fmaxf(m, ml[2 * s]);
+    for (int64_t s = first; s <= last; ++s)
+      if (!skip(s)) m = fmaxf(m, ml[2 * s]);
     float l = 0.f, x = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
+    for (int64_t s = first; s <= last; ++s) {
+      if (skip(s)) continue;
       const float wgt = exp2f((ml[2 * s] - m) * p.scale_log2);
       l = fmaf(ml[2 * s + 1], wgt, l);
-      x = fmaf(ac[(int64_t)s * kD + ch], wgt, x);
+      x = fmaf(ac[s * kD + ch], wgt, x);
     }
     o[br] = x / l;
   }
@@ -292,8 +430,13 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(const DecodeParams p
 
 template <int G, bool PAGED>
 hipError_t launch_partial(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.splits, p.Hkv, p.B);
-  hipLaunchKernelGGL((decode_partial_kernel<G, PAGED>), grid, dim3(kThreads), 0, stream, p);
+  if (PAGED && p.stream_wgs > 0) {
+    hipLaunchKernelGGL((decode_paged_balanced_kernel<G>), dim3(p.stream_wgs, p.Hkv), dim3(kThreads), 0,
+                       stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_partial_kernel<G, PAGED>), dim3(p.splits, p.Hkv, p.B), dim3(kThreads), 0,
+                       stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -343,7 +486,20 @@ void* noalloc_scratch() {
 }
 
 hipError_t launch_decode_v2_paged(const DecodeParams& p, hipStream_t stream) {
-  return launch_step<true>(p, stream);
+  // Uneven lengths would leave the per-sequence splits uneven too (the longest sequences' pieces
+  // forming the tail), so the blocks of all sequences are dealt evenly to as many workgroups as
+  // the chip holds at once (2 per CU, 1 for G = 16, whose registers allow one wave per SIMD),
+  // within the partial rows the workspace has: 2P (NW + B) <= 2P B splits.
+  DecodeParams q = p;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  const int G = 2 * p.P / p.Hkv;
+  const int64_t resident = (int64_t)cus * (G == 16 ? 1 : 2) * kPagedRounds;
+  const int64_t nw = (resident + p.Hkv - 1) / p.Hkv;
+  const int64_t cap = (int64_t)p.B * (p.splits - 1);
+  q.stream_wgs = (int)std::min<int64_t>(std::min<int64_t>(nw, cap), INT32_MAX);
+  return launch_step<true>(q, stream);
 }
 
 }  // namespace da

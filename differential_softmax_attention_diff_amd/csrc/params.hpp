@@ -110,6 +110,9 @@ struct DecodeParams {
   int32_t max_blocks;
   int32_t page_shift;          // log2(page_size)
   int32_t num_pages;
+  // Paged cache only: > 0 deals all sequences' blocks evenly to this many workgroups per KV
+  // head (partials at [2P, stream_wgs + B] rows); 0 splits every sequence into `splits` pieces.
+  int32_t stream_wgs;
 };
 
 // One V1 decode step: split-K partial pass + combine pass (norm and scale in the combine).

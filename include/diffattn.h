@@ -254,9 +254,13 @@ da_status diffattn_decode_noalloc(da_tensor q1, da_tensor q2, da_tensor kcache, 
  *   seq_lens    : int32 [B], each in 1 .. max_len (device data: not checked on the host; values
  *                 are clamped to [0, max_len] and page indices to [0, num_pages), so a bad entry
  *                 gives wrong values but no access outside the buffers; a length of 0 gives NaN)
- *   max_len     : host-side bound on seq_lens (<= max_blocks * page_size); sizes the split-K
- *                 grid and the workspace, diffattn_decode_workspace_bytes(B, P, Hkv, max_len, D,
- *                 num_splits) bytes.
+ *   max_len     : host-side bound on seq_lens (<= max_blocks * page_size); sizes the
+ *                 workspace, diffattn_decode_workspace_bytes(B, P, Hkv, max_len, D, num_splits)
+ *                 bytes, which hold S pieces per sequence (S as for diffattn_decode with
+ *                 L = max_len).  With S >= 2 the blocks of all sequences, whatever their lengths,
+ *                 are dealt evenly to min(W, B (S - 1)) workgroups per KV head, W being what the
+ *                 GPU holds at once; with S = 1 (num_splits = 1, or max_len <= 256) each
+ *                 sequence is one piece.
  *   page_size   : a power of two, 1 .. 65536.
  *
  * Supported: D == 128, dtype DA_BF16, P % Hkv == 0, 2P / Hkv <= 16.
