@@ -131,6 +131,7 @@ def test_paged_max_len_beyond_every_sequence(da):
     ([20000, 1, 1, 1, 1, 1, 1, 1], 0),        # one long sequence spread over many workgroups
     ([256, 512, 257, 255, 4096, 33], 0),      # block edges
     ([3000, 100, 5000, 700, 2000, 64], 2),    # 6 workgroups per KV head: runs cross sequences
+    (list(np.random.default_rng(3).integers(0, 700, 300)), 0),  # 300 sequences: scans past 64 and 256
 ])
 def test_paged_balanced_partition(da, lens, splits):
     """The balanced pass on uneven lengths (max_len 1000 or the longest, so that the workspace
