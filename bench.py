@@ -30,7 +30,8 @@ FLOP and byte conventions (per launch):
 with Np = N(N+1)/2 causal query-key pairs (the window's visible pairs for the sliding window).
 timing.shader_clock_mhz_median is the AMD SMI GFX clock reading sampled during the timed steps:
 indicative only (the effective clock, counted cycles over kernel time, is what the rocprofv3
-counter summaries give); short timed regions give few samples (timing.shader_clock_samples).
+counter summaries give); a timed region too short for 20 readings (timing.shader_clock_samples)
+gives null, since a handful of readings can land on idle values.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
        [--only long|v1|v2|decode|decode_v1|swa|paged|bwd|bwd_swa|train]
@@ -94,7 +95,8 @@ SETTLE_S = 0.3   # untimed load before the warm-up steps, so that the shader clo
 
 class ClockSampler:
     """Samples the GPU's shader (GFX) clock from a background thread through AMD SMI while the
-    timed steps run; ``median_mhz`` is None where the library or the sensor is unavailable."""
+    timed steps run; ``median_mhz`` is None where the library or the sensor is unavailable, or
+    where the timed region was too short for ``MIN_SAMPLES`` readings."""
 
     def __init__(self, period_s=0.005):
         self.period_s = period_s
@@ -143,9 +145,11 @@ class ClockSampler:
                 pass
         return False
 
+    MIN_SAMPLES = 20  # a timed region of a few milliseconds gets a handful of readings, some idle
+
     @property
     def median_mhz(self):
-        return float(np.median(self.samples)) if self.samples else None
+        return float(np.median(self.samples)) if len(self.samples) >= self.MIN_SAMPLES else None
 
 
 def time_launches(fn, steps, warmup, torch, settle_s=SETTLE_S):
@@ -441,7 +445,7 @@ def bench_bwd_v1(da, torch, steps, warmup, window=0):
                      "traffic": measured_traffic(name, "bwd"),
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
-                     "kernel": "bwd_prep + bwd_dkdv + bwd_dq + bwd_lambda (whole backward)"},
+                     "kernel": "bwd_dq (with the dO prologue) + bwd_dkdv + bwd_lambda (whole backward)"},
     }
 
 

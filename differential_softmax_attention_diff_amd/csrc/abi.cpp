@@ -369,8 +369,8 @@ da_status diffattn_bwd_v1(da_tensor q1, da_tensor q2, da_tensor k1, da_tensor k2
   if (dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
   if (d != 64) return d <= 0 ? DA_ERR_SHAPE : DA_ERR_UNSUPPORTED;
   if (!(eps >= 0.f) || !std::isfinite(eps)) return DA_ERR_SHAPE;
-  // grids: (B*H, N/64) for the dK/dV and dQ kernels, (B*H, N/32) for the prep kernel
-  if ((int64_t)B * H > (int64_t)INT32_MAX || (N + 31) / 32 > kMaxGridY) return DA_ERR_UNSUPPORTED;
+  // grids: (B*H, N/128) for the dQ kernel, (B*H, N/64) for the dK/dV kernel
+  if ((int64_t)B * H > (int64_t)INT32_MAX || (N + 63) / 64 > kMaxGridY) return DA_ERR_UNSUPPORTED;
   if ((int64_t)B * H * N * 16 >= ((int64_t)1 << 32)) return DA_ERR_UNSUPPORTED;
   for (const da_tensor* t : {&q1, &q2, &k1, &k2, &v, &dy}) {
     const da_status s = check_tensor(*t, 2);

@@ -18,17 +18,18 @@
 //
 // Kernels (A_b is never stored: each kernel rebuilds the weights it needs from the scores and the
 // forward's base-2 log-sum-exp, P = exp2(s log2(e)/sqrt(d) - LSE)):
-//  * bwd_prep: 16 lanes per row: O, r, dO (stored bf16 for the MFMAs), -Dt_1, -Dt_2 and the
-//    row's share of dlambda.
+//  * bwd_dq (first): one workgroup per 128 query rows, one wave per 32 of them doing both
+//    branches.  Its prologue forms, for its rows, O, r and dO (bf16, for the MFMAs), -Dt_1, -Dt_2
+//    and the row's share of dlambda, 16 lanes per row, and stores them for the dK/dV kernel; its
+//    own operands come through LDS.  Then V dO^T is formed once for both branches while it
+//    streams K_1, K_2, V tiles: S_b^T = K_b Q_b^T, P_b^T, X^T = V dO^T, dS_b^T,
+//    dQ_b^T += K_b^T dS_b^T.
 //  * bwd_dkdv: one 256-thread workgroup per 64 keys of a head, one wave per 16 of them doing
 //    both branches.  Each wave keeps its keys' K_1, K_2 and V as MFMA operands in registers and
 //    streams 32-row query tiles (Q_1, Q_2, dO, LSE, -Dt) through LDS: S_b = Q_b K_b^T and one
 //    X = dO V^T for both branches on 16x16x32 bf16 MFMAs, P_b, dS_b, then dV^T += dO^T (P_1 -
 //    lambda P_2) once and dK_b^T += Q_b^T dS_b, the transposed operands read by
 //    ds_read_b64_tr_b16.  The accumulator layout feeds the next product directly.
-//  * bwd_dq: one workgroup per 128 query rows, one wave per 32 of them doing both branches, so
-//    that V dO^T is formed once for both; streaming K_1, K_2, V tiles: S_b^T = K_b Q_b^T, P_b^T,
-//    X^T = V dO^T, dS_b^T, dQ_b^T += K_b^T dS_b^T.
 //  * bwd_lambda: per head, the sum of the rows' dlambda shares (one 1024-thread workgroup, fixed
 //    order) and the four vector gradients.
 #include <type_traits>
@@ -50,10 +51,9 @@ __device__ __forceinline__ float lam_of(const BwdParams& p, int h, int lane) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// prep: dO through the norm, -Dt_b, dlambda shares
-// 16 lanes per row (8 of its 2d channels each), four rows per wavefront pass, two passes
-constexpr int kPrepRowsPerWave = 8;
-constexpr int kPrepRowsPerBlock = kPrepRowsPerWave * (kThreads / 64);
+// prep (in the dQ kernel's prologue): dO through the norm, -Dt_b, dlambda shares; 16 lanes per
+// row (8 of its 2d channels each), four rows per wavefront pass, eight passes for a wave's rows
+constexpr int kPrepGroup = 2;  // passes whose loads are issued together
 
 // sum over the 16 lanes that share a row (xor partners stay inside the group)
 __device__ __forceinline__ float row16_sum(float x) {
@@ -62,75 +62,69 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const BwdParams p) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int sub = lane & 15;
-  const int bh = blockIdx.x;
-  const int b = bh / p.H, h = bh % p.H;
-  const float lam = lam_of(p, h, lane);
-  const int64_t BHN = (int64_t)p.B * p.H * p.N;
+// One row of the prep pass, 16 lanes per row (lane sub holds channels 8 sub .. 8 sub + 7):
+// O = O_1 - lambda O_2, r = 1/rms(O), dO = g r dy - g r^3 (O . dy) O / 2d rounded to bf16 (dq),
+// -Dt_1 = -dO . O_1 and -Dt_2 = -dO . O_2 from the rounded dO, and -dO . O_2 from the unrounded
+// one (the row's share of dlambda).  prep_load reads the row's stash and dy (row rc must be a
+// valid row), prep_row does the arithmetic.
+struct PrepIn {
+  f32x4 a1l, a1h, a2l, a2h;
+  u32x4 yw;
+};
+__device__ __forceinline__ PrepIn prep_load(const BwdParams& p, int b, int h, int64_t r, int rc, int sub,
+                                            int64_t BHN) {
+  const float* o1 = p.stash_o + r * kDV + 8 * sub;
+  const float* o2 = p.stash_o + (BHN + r) * kDV + 8 * sub;
+  const bf16* dy = static_cast<const bf16*>(p.dy) + b * p.sdy.sb + h * p.sdy.sh + (int64_t)rc * p.sdy.sn + 8 * sub;
+  // read once: non-temporal
+  PrepIn in;
+  in.a1l = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o1));
+  in.a1h = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o1 + 4));
+  in.a2l = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o2));
+  in.a2h = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o2 + 4));
+  in.yw = load16_nt(dy);
+  return in;
+}
+__device__ __forceinline__ void prep_row(const BwdParams& p, const PrepIn& in, float lam, bf16x8& dq,
+                                         float& nd1, float& nd2, float& ndl) {
+  const f32x4 a1l = in.a1l, a1h = in.a1h, a2l = in.a2l, a2h = in.a2h;
+  const u32x4 yw = in.yw;
+  float a1[8], a2[8], y[8], x[8];
 #pragma unroll
-  for (int it = 0; it < kPrepRowsPerWave / 4; ++it) {
-    const int row = blockIdx.y * kPrepRowsPerBlock + w * kPrepRowsPerWave + 4 * it + (lane >> 4);
-    // rows past N compute on row N-1 (so every lane of a group takes part) and store nothing
-    const int rc = min(row, p.N - 1);
-    const int64_t r = (int64_t)bh * p.N + rc;
-    const float* o1 = p.stash_o + r * kDV + 8 * sub;
-    const float* o2 = p.stash_o + (BHN + r) * kDV + 8 * sub;
-    const bf16* dy = static_cast<const bf16*>(p.dy) + b * p.sdy.sb + h * p.sdy.sh + (int64_t)rc * p.sdy.sn + 8 * sub;
-    // read once: non-temporal
-    const f32x4 a1l = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o1));
-    const f32x4 a1h = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o1 + 4));
-    const f32x4 a2l = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o2));
-    const f32x4 a2h = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o2 + 4));
-    const u32x4 yw = load16_nt(dy);
-    float a1[8], a2[8], y[8], x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a1[i] = a1l[i]; a1[4 + i] = a1h[i];
-      a2[i] = a2l[i]; a2[4 + i] = a2h[i];
-      y[2 * i] = bf16_lo(yw[i]);
-      y[2 * i + 1] = bf16_hi(yw[i]);
-    }
-    float ss = 0.f, dot = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[i] = a1[i] - lam * a2[i];
-      ss = fmaf(x[i], x[i], ss);
-      dot = fmaf(x[i], y[i], dot);
-    }
-    ss = row16_sum(ss);
-    dot = row16_sum(dot);
-    const float rr = rsqrtf(ss * (1.f / kDV) + p.eps);
-    const float k1 = p.g * rr, k2 = p.g * rr * rr * rr * dot * (1.f / kDV);
-    bf16x8 dq;
-    float e1 = 0.f, e2 = 0.f, g2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float d = k1 * y[i] - k2 * x[i];
-      dq[i] = (bf16)d;
-      // Dt_b from the rounded dO the MFMAs use, so that c_b Dt_b equals the row sum of P_b * dP_b
-      // that they form (the softmax Jacobian's subtraction then cancels what it should)
-      const float dr = (float)dq[i];
-      e1 = fmaf(dr, a1[i], e1);
-      e2 = fmaf(dr, a2[i], e2);
-      g2 = fmaf(d, a2[i], g2);
-    }
-    e1 = row16_sum(e1);
-    e2 = row16_sum(e2);
-    g2 = row16_sum(g2);
-    if (row < p.N) {
-      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.d_o) + r * kDV + 8 * sub) = dq;
-      if (sub == 0) {
-        // minus the row terms without the branch factor: D_b = c_b * Dt_b with Dt_b = dO . O_b,
-        // c_1 = 1, c_2 = -lambda (the consumers start an accumulator at -Dt_b)
-        p.lse_d[2 * BHN + r] = -e1;
-        p.lse_d[3 * BHN + r] = -e2;
-        p.dl_row[r] = -g2;                   // this row's share of dlambda (unrounded dO)
-      }
-    }
+  for (int i = 0; i < 4; ++i) {
+    a1[i] = a1l[i]; a1[4 + i] = a1h[i];
+    a2[i] = a2l[i]; a2[4 + i] = a2h[i];
+    y[2 * i] = bf16_lo(yw[i]);
+    y[2 * i + 1] = bf16_hi(yw[i]);
   }
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[i] = a1[i] - lam * a2[i];
+    ss = fmaf(x[i], x[i], ss);
+    dot = fmaf(x[i], y[i], dot);
+  }
+  ss = row16_sum(ss);
+  dot = row16_sum(dot);
+  const float rr = rsqrtf(ss * (1.f / kDV) + p.eps);
+  const float k1 = p.g * rr, k2 = p.g * rr * rr * rr * dot * (1.f / kDV);
+  float e1 = 0.f, e2 = 0.f, g2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float d = k1 * y[i] - k2 * x[i];
+    dq[i] = (bf16)d;
+    // Dt_b from the rounded dO the MFMAs use, so that c_b Dt_b equals the row sum of P_b * dP_b
+    // that they form (the softmax Jacobian's subtraction then cancels what it should)
+    const float dr = (float)dq[i];
+    e1 = fmaf(dr, a1[i], e1);
+    e2 = fmaf(dr, a2[i], e2);
+    g2 = fmaf(d, a2[i], g2);
+  }
+  // minus the row terms without the branch factor: D_b = c_b * Dt_b with Dt_b = dO . O_b,
+  // c_1 = 1, c_2 = -lambda (the consumers start an accumulator at -Dt_b)
+  nd1 = -row16_sum(e1);
+  nd2 = -row16_sum(e2);
+  ndl = -row16_sum(g2);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -414,7 +408,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   constexpr int BR = 128;                      // query rows per workgroup (32 per wave)
   // (both branches in one wave share X^T = V dO^T: 24 MFMAs per key tile for the two branches
   // instead of 32, at 2 waves/SIMD instead of 3; measured 6 % faster for the whole backward)
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE];
+  // (+ 1 KB: the prologue's -Dt_1, -Dt_2 of the workgroup's rows, behind its 32 KB dO tile)
+  static_assert(2 * STAGE >= 4 * 32 * kDV, "the prologue's dO tile fits the stage buffers");
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * STAGE + 512];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -443,22 +439,66 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
     const bf16* qb2 = static_cast<const bf16*>(p.q2) + b * p.sq2.sb + h * p.sq2.sh;
     const __amdgpu_buffer_rsrc_t rq1 = make_rsrc(qb1, (uint32_t)(N * p.sq1.sn * 2));
     const __amdgpu_buffer_rsrc_t rq2 = make_rsrc(qb2, (uint32_t)(N * p.sq2.sn * 2));
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<const char*>(p.d_o) + (int64_t)bh * N * kDV * 2,
-                                                (uint32_t)(N * kDV * 2));
 #pragma unroll
     for (int t = 0; t < kD / 16; ++t) {
       qf1[t] = __builtin_bit_cast(bf16x8, bload16(rq1, (uint32_t)(qrow * p.sq1.sn * 2) + 32 * t + 16 * hh));
       qf2[t] = __builtin_bit_cast(bf16x8, bload16(rq2, (uint32_t)(qrow * p.sq2.sn * 2) + 32 * t + 16 * hh));
     }
+    // dO through the norm for this wave's 32 rows (the backward's first step, done where the rows
+    // are used first): 4 rows per pass, 16 lanes per row; dO, -Dt_1, -Dt_2 and the dlambda share
+    // go to memory for the dK/dV kernel, and through LDS into this wave's operand layout
+    bf16* do_lds = smem + w * (32 * kDV);                                   // [32][128] bf16
+    float* dt_lds = reinterpret_cast<float*>(smem + 4 * 32 * kDV) + w * 64;  // [32][2]
+    {
+      const int sub = lane & 15;
+#pragma unroll
+      for (int half = 0; half < 8 / kPrepGroup; ++half) {
+      // the loads of kPrepGroup passes, then their arithmetic (2 measured best of 1, 2, 4, 8)
+      PrepIn in[kPrepGroup];
+#pragma unroll
+      for (int j = 0; j < kPrepGroup; ++j) {
+        const int row = wrow + 4 * (kPrepGroup * half + j) + (lane >> 4);
+        const int rc = min(row, N - 1);
+        in[j] = prep_load(p, b, h, (int64_t)bh * N + rc, rc, sub, BHN);
+      }
+#pragma unroll
+      for (int j = 0; j < kPrepGroup; ++j) {
+        const int it = kPrepGroup * half + j;
+        const int lr = 4 * it + (lane >> 4);  // row within the wave
+        const int row = wrow + lr;
+        // rows past N compute on row N-1 (so every lane of a group takes part) and store nothing
+        const int rc = min(row, N - 1);
+        const int64_t r = (int64_t)bh * N + rc;
+        bf16x8 d8;
+        float nd1, nd2, ndl;
+        prep_row(p, in[j], lam, d8, nd1, nd2, ndl);
+        *reinterpret_cast<bf16x8*>(do_lds + lr * kDV + 8 * sub) = d8;
+        if (sub == 0) {
+          dt_lds[2 * lr] = nd1;
+          dt_lds[2 * lr + 1] = nd2;
+        }
+        if (row < N) {
+          *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.d_o) + r * kDV + 8 * sub) = d8;
+          if (sub == 0) {
+            p.lse_d[2 * BHN + r] = nd1;
+            p.lse_d[3 * BHN + r] = nd2;
+            p.dl_row[r] = ndl;
+          }
+        }
+      }
+      }
+    }
+    __syncthreads();
 #pragma unroll
     for (int t = 0; t < kDV / 16; ++t)
-      of[t] = __builtin_bit_cast(bf16x8, bload16(ro, (uint32_t)(qrow * kDV * 2) + 32 * t + 16 * hh));
+      of[t] = *reinterpret_cast<const bf16x8*>(do_lds + c * kDV + 16 * t + 8 * hh);
+    ndd1 = dt_lds[2 * c];
+    ndd2 = dt_lds[2 * c + 1];
+    __syncthreads();  // every wave has its operands before the tile loads reuse the buffers
     if (qrow < N) {
       const int64_t r = (int64_t)bh * N + qrow;
       lse1 = p.lse_d[r];
       lse2 = p.lse_d[BHN + r];
-      ndd1 = p.lse_d[2 * BHN + r];
-      ndd2 = p.lse_d[3 * BHN + r];
     }
     __builtin_amdgcn_s_waitcnt(0);
   }
@@ -657,14 +697,12 @@ __global__ __launch_bounds__(kLambdaThreads) void bwd_lambda_kernel(const BwdPar
 
 hipError_t launch_bwd_v1(const BwdParams& p, hipStream_t stream) {
   BwdParams q = p;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3(p.B * p.H, (p.N + kPrepRowsPerBlock - 1) / kPrepRowsPerBlock),
-                     dim3(kThreads), 0, stream, q);
+  q.n_row_blocks = (p.N + 63) / 64;
+  // dQ first: its workgroups also form dO and the row terms the dK/dV kernel reads
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.B * p.H, (p.N + 127) / 128), dim3(kThreads), 0, stream, q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  q.n_row_blocks = (p.N + 63) / 64;
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.B * p.H, q.n_row_blocks), dim3(kThreads), 0, stream, q);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.B * p.H, (p.N + 127) / 128), dim3(kThreads), 0, stream, q);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_lambda_kernel, dim3(p.H), dim3(kLambdaThreads), 0, stream, q);
   return hipGetLastError();

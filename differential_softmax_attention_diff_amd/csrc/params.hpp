@@ -79,9 +79,9 @@ struct BwdParams {
   float eps;
   float g;               // 1 - lambda_init
   const float* stash_o;  // [2, B, H, N, 2d] from the training forward
-  float* lse_d;          // [4, B, H, N]: LSE_1, LSE_2 (forward, base 2), -Dt_1, -Dt_2 (prep)
-  void* d_o;             // [B, H, N, 2d] bf16: upstream gradient through the norm (prep)
-  float* dl_row;         // [B, H, N]: each row's share of dlambda (prep)
+  float* lse_d;          // [4, B, H, N]: LSE_1, LSE_2 (forward, base 2), -Dt_1, -Dt_2 (dQ prologue)
+  void* d_o;             // [B, H, N, 2d] bf16: upstream gradient through the norm (dQ prologue)
+  float* dl_row;         // [B, H, N]: each row's share of dlambda (dQ prologue)
   LambdaArgs lam;
   float* dlq1;           // [H, dl] lambda-vector gradients
   float* dlk1;
