@@ -162,9 +162,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(const BwdParams p) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;       // MFMA 16x16x32: column / row group
-  const int bh = blockIdx.x;
+  int bh, kb;
+  chunked_block(p.head_chunk, p.n_row_blocks, bh, kb);  // heads in chunks, see chunked_block
   const int b = bh / p.H, h = bh % p.H;
-  const int key0 = (int)blockIdx.y * 64;          // heaviest (earliest keys) first
+  const int key0 = kb * 64;                       // heaviest (earliest keys) first
   const int kw = key0 + 16 * w;                   // this wave's 16 keys, both branches
   const int N = p.N;
   const float lam = lam_of(p, h, lane);
@@ -416,11 +417,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, hh = lane >> 5;
-  const int bh = blockIdx.x;
-  const int b = bh / p.H, h = bh % p.H;
   const int N = p.N;
   const int nrb = (N + BR - 1) / BR;
-  const int rb = nrb - 1 - (int)blockIdx.y;   // heaviest first
+  int bh, rb;
+  chunked_block(p.head_chunk, nrb, bh, rb);  // heads in chunks, see chunked_block
+  rb = nrb - 1 - rb;                         // heaviest first
+  const int b = bh / p.H, h = bh % p.H;
   const int row0 = rb * BR;
   const int wrow = row0 + 32 * w;
   const float lam = lam_of(p, h, lane);
@@ -698,6 +700,8 @@ __global__ __launch_bounds__(kLambdaThreads) void bwd_lambda_kernel(const BwdPar
 hipError_t launch_bwd_v1(const BwdParams& p, hipStream_t stream) {
   BwdParams q = p;
   q.n_row_blocks = (p.N + 63) / 64;
+  // a head's streamed tiles: Q_1, Q_2, dO and four row terms (dK/dV); K_1, K_2, V (dQ)
+  q.head_chunk = head_chunk((int64_t)p.B * p.H, (int64_t)p.N * (2 * kD * 2 + kDV * 2 + 16));
   // dQ first: its workgroups also form dO and the row terms the dK/dV kernel reads
   hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.B * p.H, (p.N + 127) / 128), dim3(kThreads), 0, stream, q);
   hipError_t e = hipGetLastError();

@@ -63,4 +63,20 @@ __device__ __forceinline__ u32x4 load16_nt(const void* p) {
 
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Workgroup order over (head, item) for a grid of x = heads, y = items per head.  Blocks are
+// dealt to the 8 XCDs round-robin by linear index; the heads go in chunks of head_chunk (a
+// multiple of 8, or all of them; the last chunk may be short), and within a chunk the items go
+// in order with the heads running fastest, so that every item of one head lands on the same XCD
+// (the head's tiles are shared through one L2) and the tiles that the running workgroups stream
+// at once stay within the heads of one chunk.  Callers number the items heaviest first.
+__device__ __forceinline__ void chunked_block(int head_chunk, int n_items, int& head, int& item) {
+  const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t csz = (int64_t)head_chunk * n_items;
+  const int chunk = (int)(lin / csz);
+  const int cn = min(head_chunk, (int)gridDim.x - chunk * head_chunk);
+  const int j = (int)(lin - chunk * csz);
+  item = j / cn;
+  head = chunk * head_chunk + j % cn;
+}
+
 }  // namespace da

@@ -38,7 +38,7 @@ struct PrefillParams {
   int32_t norm;          // V1: apply RMS norm + (1 - lambda_init) scale
   int32_t n_row_blocks;  // query row blocks per (batch, head group)
   int32_t pairs_per_kv;  // V2: P / Hkv
-  int32_t group_heads;   // V1: issue the heads 8 at a time (one per XCD), see the prefill kernel
+  int32_t head_chunk;    // V1: heads whose row blocks are issued together (see chunked_block)
   float scale_log2;      // log2(e) / sqrt(d)
   float scale;           // 1 / sqrt(d)
   float eps;
@@ -74,6 +74,7 @@ struct BwdParams {
   int32_t causal;
   int32_t window;        // causal sliding window of the forward (0: none)
   int32_t n_row_blocks;  // 64-key blocks of the dK/dV kernel
+  int32_t head_chunk;    // heads whose blocks are issued together (see chunked_block)
   float scale;           // 1 / sqrt(d)
   float scale_log2;      // log2(e) / sqrt(d)
   float eps;

@@ -81,23 +81,17 @@ void prefill_kernel(const PrefillParams p) {
   const int rh = w & 1;      // row half
   const int c = lane & 31;
   const int hh = lane >> 5;
-  // Blocks are dealt to the 8 XCDs round-robin by linear index and blockIdx.x runs fastest, so
-  // every row block of one head (when 8 divides B*H) lands on the same XCD: a head's K/V is
-  // shared through one L2.  Row blocks go heaviest first over all heads, which keeps the causal
-  // tail short (a head-major order measured slower despite 6x less HBM fetch).  Long sequences
-  // (group_heads) take the
-  // heads 8 at a time instead, one per XCD, heaviest row block first within the group: each XCD
-  // then streams one head's K/V at a time, and a group's tail is short next to its thousands of
-  // row blocks (at N = 128K 4.5 % faster; at N = 4K the grouped order's tail cost 9 %).
-  int rb = p.n_row_blocks - 1 - (int)blockIdx.y;  // heaviest row block first
-  int hx = blockIdx.x;
-  if (p.group_heads) {
-    const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    const int64_t gsz = 8 * (int64_t)p.n_row_blocks;
-    const int j = (int)(lin % gsz);
-    rb = p.n_row_blocks - 1 - j / 8;
-    hx = (int)(lin / gsz) * 8 + j % 8;
-  }
+  // Heads in chunks (chunked_block), heaviest row block first within a chunk: every row block of
+  // one head lands on the same XCD (its K/V shared through one L2), heaviest first keeps the
+  // causal tail short (a head-major order measured slower despite 6x less HBM fetch), and the
+  // chunk bounds the K/V that the running workgroups stream at once to what the last-level cache
+  // holds.  Without chunks, 256 heads at N = 4K (512 MB of K/V) ran 45 % slower than in chunks of
+  // 64, from HBM; long sequences take 8 heads at a time, one per XCD, so that each XCD streams one
+  // head's K/V (at N = 128K 4.5 % faster than all heads at once; a chunk's tail is short next to
+  // its thousands of row blocks).
+  int rb, hx;
+  chunked_block(p.head_chunk, p.n_row_blocks, hx, rb);
+  rb = p.n_row_blocks - 1 - rb;  // heaviest row block first
   const int row0 = rb * BM;
   const int wrow = row0 + 32 * rh;
   const int N = p.N;
@@ -428,7 +422,7 @@ void prefill_kernel(const PrefillParams p) {
 hipError_t launch_v1_bf16(const PrefillParams& p, hipStream_t stream) {
   PrefillParams q = p;
   q.n_row_blocks = (p.N + 63) / 64;
-  q.group_heads = ((p.B * p.heads) % 8 == 0 && q.n_row_blocks >= 512) ? 1 : 0;
+  q.head_chunk = head_chunk((int64_t)p.B * p.heads, (int64_t)p.N * (2 * 64 + kDV) * 2);  // K1, K2, V
   const dim3 grid(p.B * p.heads, q.n_row_blocks);
   hipLaunchKernelGGL((prefill_kernel<64, kStagesV1>), grid, dim3(kThreads), 0, stream, q);
   return hipGetLastError();
