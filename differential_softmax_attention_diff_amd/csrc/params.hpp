@@ -38,7 +38,7 @@ struct PrefillParams {
   int32_t norm;          // V1: apply RMS norm + (1 - lambda_init) scale
   int32_t n_row_blocks;  // query row blocks per (batch, head group)
   int32_t pairs_per_kv;  // V2: P / Hkv
-  int32_t head_chunk;    // V1: heads whose row blocks are issued together (see chunked_block)
+  int32_t head_chunk;    // heads (V2: KV heads) whose row blocks are issued together (chunked_block)
   float scale_log2;      // log2(e) / sqrt(d)
   float scale;           // 1 / sqrt(d)
   float eps;

@@ -35,9 +35,9 @@
 //    through the scalar cache, so that no vector-memory wait sits between a tile's DMA and the
 //    previous tile's products.
 //  * Causal and sliding-window masks apply to the tiles that cross the diagonal, the window's
-//    lower edge or the ragged end only.  Row blocks are issued heaviest first; every row block of
-//    all pairs over one KV head lands on one XCD (blockIdx.x runs fastest, XCDs are dealt round
-//    robin), so a KV head's K/V is shared through one L2.
+//    lower edge or the ragged end only.  Row blocks are issued heaviest first within chunks of KV
+//    heads sized to the last-level cache; every row block of all pairs over one KV head lands on
+//    one XCD (XCDs are dealt round robin), so a KV head's K/V is shared through one L2.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -128,15 +128,27 @@ void prefill_v2_kernel(const PrefillParams p) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
-  const int rb = p.n_row_blocks - 1 - (int)blockIdx.y;  // heaviest row block first
+  // Order: the (batch, KV head)s in chunks of head_chunk (see chunked_block); within a chunk the
+  // row blocks heaviest first, then the pair within its KV head, the KV head running fastest, so
+  // that every block over one KV head lands on the same XCD
+  int rb, pi, kv;
+  {
+    const int bk = p.B * p.Hkv;
+    const int ppk = p.pairs_per_kv;
+    const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t csz = (int64_t)p.head_chunk * ppk * p.n_row_blocks;
+    const int chunk = (int)(lin / csz);
+    const int cn = min(p.head_chunk, bk - chunk * p.head_chunk);  // the last may be short
+    const int j = (int)(lin - chunk * csz);
+    rb = p.n_row_blocks - 1 - j / (cn * ppk);  // heaviest row block first
+    const int r = j % (cn * ppk);
+    pi = r / cn;
+    kv = chunk * p.head_chunk + r % cn;
+  }
   const int row0 = rb * 64;
   const int wrow = row0 + 16 * w;
   const int N = p.N;
-  // blockIdx.x = (pair within its KV head, b, KV head) with the KV head fastest
-  const int bk = p.B * p.Hkv;
-  const int pi = blockIdx.x / bk;
-  const int rem = blockIdx.x % bk;
-  const int b = rem / p.Hkv, kvh = rem % p.Hkv;
+  const int b = kv / p.Hkv, kvh = kv % p.Hkv;
   const int qh = kvh * p.pairs_per_kv + pi;
 
   // Q^T operands of both heads: lane (n, g) holds row wrow + n, columns 32 ks + 8 g .. + 7
@@ -411,6 +423,7 @@ hipError_t launch_v2_bf16(const PrefillParams& p, hipStream_t stream) {
   PrefillParams q = p;
   q.pairs_per_kv = p.heads / p.Hkv;
   q.n_row_blocks = (p.N + 63) / 64;
+  q.head_chunk = head_chunk((int64_t)p.B * p.Hkv, (int64_t)p.N * 2 * kDV * 2);  // K, V of a KV head (D = 128)
   hipLaunchKernelGGL(v2_values_kernel, dim3((p.N + kSBN - 1) / kSBN, p.B * p.Hkv), dim3(kThreads), 0, stream, q);
   const dim3 grid(p.B * p.heads, q.n_row_blocks);
   hipLaunchKernelGGL(prefill_v2_kernel, grid, dim3(kThreads), 0, stream, q);

@@ -1,6 +1,6 @@
 """Workgroup order with the heads in chunks.  When the heads' streamed tiles exceed about half the
-last-level cache, the V1 prefill and the backward issue the heads in chunks (multiples of 8, the
-last one shorter), heaviest row block first within a chunk.  The order decides only where and
+last-level cache, the V1 prefill, the V2 prefill (over KV heads) and the backward issue the heads
+in chunks (multiples of 8, the last one shorter), heaviest row block first within a chunk.  The order decides only where and
 when a block runs, never what it computes: a call over 12 heads at N = 32K + 5 (the prefill's
 201 MB of K/V and the backward's 208 MB of tiles give chunks of 8 and 4 heads) must equal, bit for
 bit, the same heads run one call each (one head: one chunk).  Per-row correctness is the parity
@@ -58,7 +58,9 @@ def _head(x, b, h):
 def test_chunk_sizes_of_this_shape():
     assert _chunk(B * H, N * (2 * 64 + 128) * 2) == 8           # prefill: chunks of 8 and 4
     assert _chunk(B * H, N * (2 * 64 * 2 + 128 * 2 + 16)) == 8  # backward: chunks of 8 and 4
+    assert _chunk(B * H, N * 2 * 128 * 2) == 8                  # V2, 12 KV heads: 8 and 4
     assert _chunk(64, 4096 * 512) == 64                         # the 4K workload: one chunk
+    assert _chunk(16, 8192 * 512) == 16                         # the V2 8K workload: one chunk
 
 
 def test_v1_prefill_chunked_equals_per_head(da, inputs):
@@ -96,3 +98,28 @@ def test_v1_backward_chunked_equals_per_head(da, inputs):
             for k in ("dq1", "dq2", "dk1", "dk2", "dv"):
                 assert torch.equal(g1[k][0, 0], g[k][b, h]), (k, b, h)
     log(f"  backward over {B * H} heads at N={N} equals the per-head calls bit for bit")
+
+
+def test_v2_prefill_chunked_equals_per_kv_head(da):
+    """V2 over B * Hkv = 12 KV heads of 2 pairs each at N = 32K + 5 (chunks of 8 and 4 KV heads)
+    against one call per (batch, KV head) with its two pairs."""
+    import torch
+
+    P, Hkv = 8, 4
+    ppk = P // Hkv
+    t = wl.make_v2(B, P, Hkv, N, 128, "bf16", seed=41, layers=(LAYER,))
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    lam = dev_lambda(t["lambda"][LAYER])
+    del t
+    whole = da.diffattn_fwd_v2(q[:, 0::2], q[:, 1::2], k, v, *lam, layer=LAYER)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for g in range(Hkv):
+            ps = slice(g * ppk, (g + 1) * ppk)
+            q1 = q[b:b + 1, 0::2][:, ps]
+            q2 = q[b:b + 1, 1::2][:, ps]
+            one = da.diffattn_fwd_v2(q1, q2, k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
+                                     *[a[ps] for a in lam], layer=LAYER)
+            torch.cuda.synchronize()
+            assert torch.equal(one[0], whole[b, ps]), (b, g)
+    log(f"  V2 prefill over {B * Hkv} KV heads at N={N} equals the per-KV-head calls bit for bit")
