@@ -449,7 +449,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
     // dO through the norm for this wave's 32 rows (the backward's first step, done where the rows
     // are used first): 4 rows per pass, 16 lanes per row; dO, -Dt_1, -Dt_2 and the dlambda share
     // go to memory for the dK/dV kernel, and through LDS into this wave's operand layout
-    bf16* do_lds = smem + w * (32 * kDV);                                   // [32][128] bf16
+    // [32][128] bf16, 16-byte chunk k of row r at chunk k ^ (r & 15), so that the operand reads
+    // (one chunk of 32 rows at a time) spread over the banks
+    bf16* do_lds = smem + w * (32 * kDV);
     float* dt_lds = reinterpret_cast<float*>(smem + 4 * 32 * kDV) + w * 64;  // [32][2]
     {
       const int sub = lane & 15;
@@ -474,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
         bf16x8 d8;
         float nd1, nd2, ndl;
         prep_row(p, in[j], lam, d8, nd1, nd2, ndl);
-        *reinterpret_cast<bf16x8*>(do_lds + lr * kDV + 8 * sub) = d8;
+        *reinterpret_cast<bf16x8*>(do_lds + lr * kDV + 8 * (sub ^ (lr & 15))) = d8;
         if (sub == 0) {
           dt_lds[2 * lr] = nd1;
           dt_lds[2 * lr + 1] = nd2;
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < kDV / 16; ++t)
-      of[t] = *reinterpret_cast<const bf16x8*>(do_lds + c * kDV + 16 * t + 8 * hh);
+      of[t] = *reinterpret_cast<const bf16x8*>(do_lds + c * kDV + 8 * ((2 * t + hh) ^ (c & 15)));
     ndd1 = dt_lds[2 * c];
     ndd2 = dt_lds[2 * c + 1];
     __syncthreads();  // every wave has its operands before the tile loads reuse the buffers
