@@ -51,6 +51,26 @@ def _gather(t, b):
     return k, v
 
 
+def _check(got, ref):
+    """The bf16 bar on a decode output of a few sequences (reading r24): the largest error,
+    normalised by the oracle row's RMS, within 2e-2, and every element within 2e-3 of that RMS
+    beyond the bf16 rounding of the exact result (every step before the final store is fp32).  The
+    share-within-1e-2 statistic is for populations larger than a few sequences' 128-wide rows:
+    rounding the exact outputs alone can leave 2 of 1536 elements past 1e-2."""
+    st = compare.bf16_stats(got, ref, normalise=True)
+    ex = beyond_output_rounding(got, ref)
+    log(f"  stats {st}; beyond the output rounding {ex:.2e}")
+    assert st["finite"] and st["max_abs"] <= 2e-2 and ex <= 2e-3, (st, ex)
+
+
+def _within_one_step(a, b):
+    """Two bf16 results of the same step that differ only in fp32 summation order: every element
+    within one bf16 step (2^-7 of its magnitude, the larger of the two)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b))), float(np.max(np.abs(a - b)))
+
+
 def _oracle(t, layer, batches):
     lam = oracle_lambda(t["lambda"][layer], layer)
     out = []
@@ -66,23 +86,24 @@ def _oracle(t, layer, batches):
     (1, 1, 64, [64, 65, 3], 3),               # G = 2, 64-key pages, fixed splits
     (8, 1, 32, [777, 128], 1),                # G = 16, unsplit
     (4, 2, 1, [5, 40], 0),                    # one key per page
+    (4, 2, 128, [129, 640, 1], 2),            # two pages per 256-key block
+    (4, 2, 256, [300, 1000, 5], 0),           # one page per block
+    (2, 1, 1024, [2500, 77], 0),              # a block inside a page
 ])
 def test_paged_decode_against_oracle(da, P, Hkv, page, lens, splits):
     log(f"paged decode P={P} Hkv={Hkv} page={page} lens={lens} splits={splits}")
     t = wl.make_decode_paged(len(lens), P, Hkv, 128, page, lens, seed=sum(lens) + page, layers=(24,))
     got = _run(da, t, 24, splits)
     ref = _oracle(t, 24, range(len(lens)))
-    st = compare.bf16_stats(got, ref, normalise=True)
-    log(f"  stats {st}")
-    assert compare.bf16_ok(st), st
+    _check(got, ref)
 
 
 def test_paged_equals_contiguous_when_pages_are_in_order(da):
     """One sequence length for all, pages in order.  Unsplit (one piece per sequence and KV head
     on both paths): the same numbers as diffattn_decode, bit for bit.  With two splits the paged
     step deals all sequences' blocks evenly to its workgroups instead of splitting each sequence,
-    so the pieces (and the fp32 summation order) differ from the contiguous step's: equal up to
-    the bf16 output rounding."""
+    so the pieces (and the fp32 summation order) differ from the contiguous step's: every element
+    within one bf16 step."""
     import torch
 
     B, P, Hkv, L, page = 2, 4, 2, 1000, 8
@@ -103,9 +124,7 @@ def test_paged_equals_contiguous_when_pages_are_in_order(da):
         if splits == 1:
             np.testing.assert_array_equal(a, b)
         else:
-            st = compare.bf16_stats(a, b, normalise=True)
-            log(f"  two splits, paged vs contiguous: {st}")
-            assert compare.bf16_ok(st), st
+            _within_one_step(a, b)
 
 
 def test_paged_max_len_beyond_every_sequence(da):
@@ -118,11 +137,8 @@ def test_paged_max_len_beyond_every_sequence(da):
     t["block_table"] = np.pad(t["block_table"], ((0, 0), (0, 100)), constant_values=-1)
     b = _run(da, t, 24, max_len=t["block_table"].shape[1] * 16)   # 2304
     for x in (a, b):
-        st = compare.bf16_stats(x, ref, normalise=True)
-        log(f"  stats {st}")
-        assert compare.bf16_ok(st), st
-    st = compare.bf16_stats(b, a, normalise=True)
-    assert compare.bf16_ok(st), st
+        _check(x, ref)
+    _within_one_step(a, b)
 
 
 @pytest.mark.parametrize("lens,splits", [
@@ -150,9 +166,7 @@ def test_paged_balanced_partition(da, lens, splits):
     got = _run(da, t, 24, num_splits=splits, max_len=max_len)
     live = [b for b in range(len(lens)) if lens[b] > 0]
     ref = _oracle(t, 24, live)
-    st = compare.bf16_stats(got[live], ref, normalise=True)
-    log(f"  stats {st}")
-    assert compare.bf16_ok(st), st
+    _check(got[live], ref)
 
 
 @pytest.mark.timeout(900)
