@@ -78,9 +78,10 @@ __global__ __launch_bounds__(kThreads) void decode_v1_partial_kernel(const Decod
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[br][e] = 0.f;
 
-  for (int blk = k_begin; blk < k_end; blk += kKB) {
-    // this block's K1, K2 and V loads, all issued up front
-    u32x4 kf[2][4][2];
+  // A block's K1, K2 rows are loaded while the block before it finishes, into the registers its
+  // score products are done with, as soon as they are; V at the block's start
+  u32x4 kf[2][4][2];
+  auto load_k = [&](int blk) {
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
       const int key = blk + 64 * w + 16 * sb + l16;
@@ -91,6 +92,9 @@ __global__ __launch_bounds__(kThreads) void decode_v1_partial_kernel(const Decod
           kf[br][sb][t] = key < k_end ? load16_nt(kb[br] + (int64_t)key * ksn[br] + 32 * t + 8 * grp)
                                       : u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  if (k_begin < k_end) load_k(k_begin);
+  for (int blk = k_begin; blk < k_end; blk += kKB) {
     u32x4 vf[16];
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
@@ -112,6 +116,7 @@ __global__ __launch_bounds__(kThreads) void decode_v1_partial_kernel(const Decod
         if (grp == 0) sc_lds[br][kl] = valid ? s[0] : -INFINITY;
       }
     }
+    if (blk + kKB < k_end) load_k(blk + kKB);
     __syncthreads();
 
     // block softmax statistics: wavefront 0 owns branch 1, wavefront 1 branch 2

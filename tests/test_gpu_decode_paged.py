@@ -89,6 +89,8 @@ def _oracle(t, layer, batches):
     (4, 2, 128, [129, 640, 1], 2),            # two pages per 256-key block
     (4, 2, 256, [300, 1000, 5], 0),           # one page per block
     (2, 1, 1024, [2500, 77], 0),              # a block inside a page
+    (4, 1, 16, [3000, 40, 1500], 0),          # G = 8: the per-sequence splits
+    (8, 1, 16, [3000, 40, 1500], 0),          # G = 16, balanced
 ])
 def test_paged_decode_against_oracle(da, P, Hkv, page, lens, splits):
     log(f"paged decode P={P} Hkv={Hkv} page={page} lens={lens} splits={splits}")
