@@ -131,10 +131,11 @@ __device__ __forceinline__ void partial_range(const DecodeParams& p, PartialLds<
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
-  // For G <= 4 a block's K rows are loaded while the block before it finishes: into the registers
-  // its score products are done with, as soon as they are (3.5 % faster at the 32K workload); V at
-  // the block's start.  Wider groups would need more than 256 registers for it (one wave per SIMD).
-  constexpr bool kEarlyK = G <= 4;
+  // A block's K rows are loaded while the block before it finishes: into the registers its score
+  // products are done with, as soon as they are (3.5 % faster at the 32K workload); V at the
+  // block's start.  Where that would take more than 256 registers (one wave per SIMD) -- G = 8
+  // with a paged cache, G = 16 -- K is loaded at the block's start instead.
+  constexpr bool kEarlyK = G <= 4 || (G == 8 && !PAGED);
   u32x4 kf[4][4];
   auto load_k = [&](int blk, int tb) {
 #pragma unroll

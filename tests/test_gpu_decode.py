@@ -44,6 +44,7 @@ def _run_decode(da, t, layer, num_splits=0, kc=None, vc=None):
     (3, 16, 8, 5000, 0),    # the workload's head layout
     (2, 16, 8, 5000, 1),    # same, unsplit
     (1, 4, 2, 2049, 7),
+    (2, 4, 1, 3000, 2),     # G = 8 over several blocks per split
 ])
 def test_decode_full_compare(da, B, P, Hkv, L, splits):
     log(f"decode B={B} P={P} Hkv={Hkv} L={L} splits={splits}")
