@@ -68,9 +68,19 @@ KERNEL_SOURCES = {
 }
 
 
+# Headers shared by every kernel family: launch parameters, the workgroup order (head chunks)
+# and the load/store helpers, which change what a kernel reads as much as its own source does.
+SHARED_SOURCES = [os.path.join(ROOT, "differential_softmax_attention_diff_amd", "csrc", f)
+                  for f in ("params.hpp", "launch.hpp", "device_common.hpp", "tile_common.hpp")]
+
+
 def source_hash(kind: str) -> str:
-    with open(KERNEL_SOURCES[kind], "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over the kernel family's source followed by the shared headers."""
+    h = hashlib.sha256()
+    for path in [KERNEL_SOURCES[kind], *SHARED_SOURCES]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(key: str, kind: str):

@@ -7,11 +7,11 @@
 namespace da {
 
 // Heads per chunk of the workgroup order (see chunked_block): the heads' streamed tiles,
-// bytes_per_head each, split into chunks of about half the 256 MB last-level cache (the nearest
-// whole number of chunks, at least one), the chunks of equal size in multiples of 8 (one head per
-// XCD); all heads if that is more than there are.
+// bytes_per_head each, split into chunks of about a quarter of the 256 MB last-level cache (the
+// nearest whole number of chunks, at least one), the chunks of equal size in multiples of 8 (one
+// head per XCD); all heads if that is more than there are.
 inline int head_chunk(int64_t heads, int64_t bytes_per_head) {
-  constexpr int64_t kChunkBytes = int64_t(128) << 20;
+  constexpr int64_t kChunkBytes = int64_t(64) << 20;
   int64_t n = (heads * bytes_per_head + kChunkBytes / 2) / kChunkBytes;
   if (n < 1) n = 1;
   int64_t c = (heads + n - 1) / n;

@@ -1,5 +1,5 @@
-"""Workgroup order with the heads in chunks.  When the heads' streamed tiles exceed about half the
-last-level cache, the V1 prefill, the V2 prefill (over KV heads) and the backward issue the heads
+"""Workgroup order with the heads in chunks.  When the heads' streamed tiles exceed about a quarter of
+the last-level cache, the V1 prefill, the V2 prefill (over KV heads) and the backward issue the heads
 in chunks (multiples of 8, the last one shorter), heaviest row block first within a chunk.  The order decides only where and
 when a block runs, never what it computes: a call over 12 heads at N = 32K + 5 (the prefill's
 201 MB of K/V and the backward's 208 MB of tiles give chunks of 8 and 4 heads) must equal, bit for
@@ -18,9 +18,9 @@ B, H, N, LAYER = 3, 4, 32768 + 5, 9
 
 
 def _chunk(heads, bytes_per_head):
-    """The launchers' chunk size, restated (nearest whole number of 128 MB chunks, balanced,
+    """The launchers' chunk size, restated (nearest whole number of 64 MB chunks, balanced,
     rounded up to a multiple of 8)."""
-    k = 128 << 20
+    k = 64 << 20
     n = max(1, (heads * bytes_per_head + k // 2) // k)
     c = -(-heads // n)
     c = -(-c // 8) * 8
@@ -59,7 +59,7 @@ def test_chunk_sizes_of_this_shape():
     assert _chunk(B * H, N * (2 * 64 + 128) * 2) == 8           # prefill: chunks of 8 and 4
     assert _chunk(B * H, N * (2 * 64 * 2 + 128 * 2 + 16)) == 8  # backward: chunks of 8 and 4
     assert _chunk(B * H, N * 2 * 128 * 2) == 8                  # V2, 12 KV heads: 8 and 4
-    assert _chunk(64, 4096 * 512) == 64                         # the 4K workload: one chunk
+    assert _chunk(64, 4096 * 512) == 32                         # the 4K workload: two chunks
     assert _chunk(16, 8192 * 512) == 16                         # the V2 8K workload: one chunk
 
 
