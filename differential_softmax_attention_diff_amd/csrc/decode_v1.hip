@@ -33,6 +33,7 @@ constexpr int kDV = 128;   // value width
 constexpr int kKB = 256;   // keys per block (64 per wavefront)
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;
+constexpr int kCombineBatch = 8;  // split partials per branch that the combine loads at once
 
 __global__ __launch_bounds__(kThreads) void decode_v1_partial_kernel(const DecodeV1Params p) {
   __shared__ float sc_lds[2][kKB];                               // scores of the block, per branch
@@ -207,19 +208,56 @@ __global__ __launch_bounds__(kDV) void decode_v1_combine_kernel(const DecodeV1Pa
   if (p.lam.out != nullptr && b == 0 && ch == 0) p.lam.out[h] = lam;
   const int64_t row0 = ((int64_t)b * p.H + h) * 2;
   float o[2];
+  if (p.splits <= kCombineBatch) {
+    // every partial of both branches loaded at once (their loads in flight together), then
+    // merged in split order
+    float mv[2][kCombineBatch], lv[2][kCombineBatch], av[2][kCombineBatch];
 #pragma unroll
-  for (int br = 0; br < 2; ++br) {
-    const float* ml = p.ws_ml + (row0 + br) * p.splits * 2;
-    const float* ac = p.ws_acc + (row0 + br) * p.splits * kDV;
-    float m = kNegBig;
-    for (int s = 0; s < p.splits; ++s) m = fmaxf(m, ml[2 * s]);
-    float l = 0.f, x = 0.f;
-    for (int s = 0; s < p.splits; ++s) {
-      const float wgt = exp2f((ml[2 * s] - m) * p.scale_log2);
-      l = fmaf(ml[2 * s + 1], wgt, l);
-      x = fmaf(ac[(int64_t)s * kDV + ch], wgt, x);
+    for (int br = 0; br < 2; ++br) {
+      const float* ml = p.ws_ml + (row0 + br) * p.splits * 2;
+      const float* ac = p.ws_acc + (row0 + br) * p.splits * kDV;
+#pragma unroll
+      for (int s = 0; s < kCombineBatch; ++s) {
+        mv[br][s] = kNegBig;
+        lv[br][s] = av[br][s] = 0.f;
+        if (s < p.splits) {
+          mv[br][s] = ml[2 * s];
+          lv[br][s] = ml[2 * s + 1];
+          av[br][s] = ac[(int64_t)s * kDV + ch];
+        }
+      }
     }
-    o[br] = x / l;
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      float m = kNegBig;
+#pragma unroll
+      for (int s = 0; s < kCombineBatch; ++s) m = fmaxf(m, mv[br][s]);
+      float l = 0.f, x = 0.f;
+#pragma unroll
+      for (int s = 0; s < kCombineBatch; ++s) {
+        if (s < p.splits) {
+          const float wgt = exp2f((mv[br][s] - m) * p.scale_log2);
+          l = fmaf(lv[br][s], wgt, l);
+          x = fmaf(av[br][s], wgt, x);
+        }
+      }
+      o[br] = x / l;
+    }
+  } else {
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      const float* ml = p.ws_ml + (row0 + br) * p.splits * 2;
+      const float* ac = p.ws_acc + (row0 + br) * p.splits * kDV;
+      float m = kNegBig;
+      for (int s = 0; s < p.splits; ++s) m = fmaxf(m, ml[2 * s]);
+      float l = 0.f, x = 0.f;
+      for (int s = 0; s < p.splits; ++s) {
+        const float wgt = exp2f((ml[2 * s] - m) * p.scale_log2);
+        l = fmaf(ml[2 * s + 1], wgt, l);
+        x = fmaf(ac[(int64_t)s * kDV + ch], wgt, x);
+      }
+      o[br] = x / l;
+    }
   }
   const float x = o[0] - lam * o[1];
   float rs = 1.f;

@@ -35,6 +35,7 @@ constexpr int kKB = 256;  // keys per block (64 per wavefront)
 constexpr int kThreads = 256;
 constexpr float kNegBig = -1.0e30f;
 constexpr int kPagedRounds = 1;  // balanced paged pass: workgroups per resident slot
+constexpr int kCombineBatch = 8;  // partial slots per head that the combine loads at once
 
 // G = query heads per KV head (2P / Hkv): 2, 4, 8 or 16.  PAGED: the cache is a pool of pages
 // [num_pages, Hkv, page_size, D] addressed through a per-sequence block table, and every sequence
@@ -422,22 +423,64 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(const DecodeParams p
     return w * tot_blocks / p.stream_wgs == (w + 1) * tot_blocks / p.stream_wgs;
   };
   float o[2];
+  if (last - first < kCombineBatch) {
+    // every partial of both heads loaded at once (their loads in flight together), then merged
+    // in slot order
+    bool use[kCombineBatch];
+    float mv[2][kCombineBatch], lv[2][kCombineBatch], av[2][kCombineBatch];
 #pragma unroll
-  for (int br = 0; br < 2; ++br) {
-    const int hq = 2 * pair + br;
-    const float* ml = p.ws_ml + (hq * stride) * 2;
-    const float* ac = p.ws_acc + (hq * stride) * kD;
-    float m = kNegBig;
-    for (int64_t s = first; s <= last; ++s)
-      if (!skip(s)) m = fmaxf(m, ml[2 * s]);
-    float l = 0.f, x = 0.f;
-    for (int64_t s = first; s <= last; ++s) {
-      if (skip(s)) continue;
-      const float wgt = exp2f((ml[2 * s] - m) * p.scale_log2);
-      l = fmaf(ml[2 * s + 1], wgt, l);
-      x = fmaf(ac[s * kD + ch], wgt, x);
+    for (int i = 0; i < kCombineBatch; ++i) use[i] = first + i <= last && !skip(first + i);
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      const int hq = 2 * pair + br;
+      const float* ml = p.ws_ml + (hq * stride) * 2;
+      const float* ac = p.ws_acc + (hq * stride) * kD;
+#pragma unroll
+      for (int i = 0; i < kCombineBatch; ++i) {
+        const int64_t s = first + i;
+        mv[br][i] = kNegBig;
+        lv[br][i] = av[br][i] = 0.f;
+        if (use[i]) {
+          mv[br][i] = ml[2 * s];
+          lv[br][i] = ml[2 * s + 1];
+          av[br][i] = ac[s * kD + ch];
+        }
+      }
     }
-    o[br] = x / l;
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      float m = kNegBig;
+#pragma unroll
+      for (int i = 0; i < kCombineBatch; ++i) m = fmaxf(m, mv[br][i]);
+      float l = 0.f, x = 0.f;
+#pragma unroll
+      for (int i = 0; i < kCombineBatch; ++i) {
+        if (use[i]) {
+          const float wgt = exp2f((mv[br][i] - m) * p.scale_log2);
+          l = fmaf(lv[br][i], wgt, l);
+          x = fmaf(av[br][i], wgt, x);
+        }
+      }
+      o[br] = x / l;
+    }
+  } else {
+#pragma unroll
+    for (int br = 0; br < 2; ++br) {
+      const int hq = 2 * pair + br;
+      const float* ml = p.ws_ml + (hq * stride) * 2;
+      const float* ac = p.ws_acc + (hq * stride) * kD;
+      float m = kNegBig;
+      for (int64_t s = first; s <= last; ++s)
+        if (!skip(s)) m = fmaxf(m, ml[2 * s]);
+      float l = 0.f, x = 0.f;
+      for (int64_t s = first; s <= last; ++s) {
+        if (skip(s)) continue;
+        const float wgt = exp2f((ml[2 * s] - m) * p.scale_log2);
+        l = fmaf(ml[2 * s + 1], wgt, l);
+        x = fmaf(ac[s * kD + ch], wgt, x);
+      }
+      o[br] = x / l;
+    }
   }
   bf16* out = static_cast<bf16*>(p.out) + b * p.so.sb + pair * p.so.sh;
   out[ch] = (bf16)(o[0] - lam * o[1]);
