@@ -665,15 +665,31 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------------------------
 // dlambda per head and the four vector gradients
 constexpr int kLambdaThreads = 1024;
+constexpr int kLambdaBatch = 8;  // row shares per thread loaded at once
 
 __global__ __launch_bounds__(kLambdaThreads) void bwd_lambda_kernel(const BwdParams p) {
   __shared__ float part[kLambdaThreads / 64];
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // this thread's shares in the order (batch, row tid + r kLambdaThreads), loaded kLambdaBatch at a
+  // time so that their loads are in flight together, and added in that order
   float s = 0.f;
-  for (int b = 0; b < p.B; ++b) {
-    const float* dl = p.dl_row + ((int64_t)b * p.H + h) * p.N;
-    for (int i = tid; i < p.N; i += kLambdaThreads) s += dl[i];
+  const int per_b = tid < p.N ? (p.N - tid + kLambdaThreads - 1) / kLambdaThreads : 0;
+  const int tot = p.B * per_b;
+  for (int t0 = 0; t0 < tot; t0 += kLambdaBatch) {
+    float v[kLambdaBatch];
+#pragma unroll
+    for (int j = 0; j < kLambdaBatch; ++j) {
+      v[j] = 0.f;
+      const int t = t0 + j;
+      if (t < tot) {
+        const int b = t / per_b, r = t - b * per_b;
+        v[j] = p.dl_row[((int64_t)b * p.H + h) * p.N + tid + r * kLambdaThreads];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kLambdaBatch; ++j)
+      if (t0 + j < tot) s += v[j];
   }
   s = wave_sum(s);
   if (lane == 0) part[w] = s;
