@@ -74,12 +74,26 @@ SHARED_SOURCES = [os.path.join(ROOT, "differential_softmax_attention_diff_amd", 
                   for f in ("params.hpp", "launch.hpp", "device_common.hpp", "tile_common.hpp")]
 
 
+def compile_flags(kind: str) -> list:
+    """The kernel family's compile flags, without the machine-specific include paths."""
+    from differential_softmax_attention_diff_amd import _build
+
+    flags, skip = [], False
+    for f in [*_build.COMMON_FLAGS, *_build.EXTRA_FLAGS.get(os.path.basename(KERNEL_SOURCES[kind]), [])]:
+        if skip or f == "-I":
+            skip = f == "-I"
+            continue
+        flags.append(f)
+    return flags
+
+
 def source_hash(kind: str) -> str:
-    """sha256[:16] over the kernel family's source followed by the shared headers."""
+    """sha256[:16] over the kernel family's source, the shared headers and its compile flags."""
     h = hashlib.sha256()
     for path in [KERNEL_SOURCES[kind], *SHARED_SOURCES]:
         with open(path, "rb") as f:
             h.update(f.read())
+    h.update(" ".join(compile_flags(kind)).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,9 +24,14 @@ SOURCES = ["abi.cpp", "fwd_v1_f32.hip", "prefill_bf16.hip", "prefill_v2_bf16.hip
 # softmax rescales them with vector ALU ops, and AGPR-resident accumulators cost a copy per use.
 # They also never produce a NaN of their own (masked scores are -inf, exp2(-inf) = 0), so the
 # compiler may drop the NaN-quieting canonicalisations it would otherwise put before each max.
+# The V2 prefill and the backward are scheduled with the iterative ILP strategy, which interleaves
+# their MFMA and vector work more tightly within the same occupancy (1.2 % and 1.0 % faster,
+# bit-identical output; the V1 prefill measured no gain from it).
 EXTRA_FLAGS = {"prefill_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
-               "prefill_v2_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
-               "bwd_v1.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
+               "prefill_v2_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans",
+                                       "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+               "bwd_v1.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans",
+                              "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 ARCH = "gfx950"
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
