@@ -97,15 +97,23 @@ def source_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(key: str, kind: str):
-    """HBM bytes per launch from the committed counter run, or None if the kernel has changed."""
+def combined_hash(kinds) -> str:
+    """source_hash of one kernel family, or sha256[:16] over those of several (in order)."""
+    if isinstance(kinds, str):
+        return source_hash(kinds)
+    return hashlib.sha256("+".join(source_hash(k) for k in kinds).encode()).hexdigest()[:16]
+
+
+def measured_traffic(key: str, kinds):
+    """HBM bytes per launch (or step) from the committed counter run, or None if any of the
+    kernel families it covers has changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     ent = data.get(key)
-    if not ent or ent.get("source_hash") != source_hash(kind):
+    if not ent or ent.get("source_hash") != combined_hash(kinds):
         return None
     return ent.get("bytes_per_launch")
 
@@ -504,7 +512,7 @@ def bench_train_step(da, torch, steps, warmup):
                    "causal": True, "layer": layer, "dtype": "bf16 in, fp32 gradients"},
         "roofline": {"bound": "mfma", "achieved": round(tf_alg, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf_alg / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic("v1_train_step_4k", ("prefill", "bwd")),
                      "executed_mfma_tflops": round(tf_exec, 2),
                      "executed_mfma_frac": round(tf_exec / PEAK_BF16_TFLOPS, 4),
                      "kernel": "training forward (with stash) + backward"},
